@@ -1,0 +1,114 @@
+// Device-side helpers shared by the forward kernels: element types, the
+// workgroup -> (sequence, head, query tile) schedule, and the window test.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_params.h"
+
+namespace fa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <typename T> struct Vec8;
+template <> struct Vec8<__bf16> { typedef bf16x8 type; };
+template <> struct Vec8<_Float16> { typedef f16x8 type; };
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }    // RNE
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }  // RNE
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// One query tile of one (sequence, query head).
+struct Tile {
+  int b, h, qt;       // batch or sequence index, query head, tile index within the sequence
+  int64_t q_row0;     // first global row of this sequence in q / o (TND), else 0
+  int64_t kv_row0;    // first global row of this sequence in k / v (TND), else 0
+  int sq, skv;        // rows of this sequence
+  bool valid;
+};
+
+// Workgroups are dealt round-robin over the 8 XCDs (each with its own L2).
+// Renumber them so each XCD receives one contiguous run of the linear tile
+// order, in which the query tiles of one head are adjacent: a head's K/V then
+// stays within one XCD's L2.
+__device__ __forceinline__ int xcd_linear_id(int bid, int grid) {
+  const int x = bid & 7, i = bid >> 3;
+  const int per = grid >> 3, rem = grid & 7;
+  return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+}
+
+__device__ __forceinline__ Tile map_tile(const Params& p, int bid) {
+  Tile t;
+  const int lin = xcd_linear_id(bid, p.num_wg);
+  const int tph = p.tiles_per_head;
+  if (!p.varlen) {
+    const int bh = lin / tph;
+    const int r = lin - bh * tph;
+    t.b = bh / p.nq;
+    t.h = bh - t.b * p.nq;
+    t.qt = p.reverse_tiles ? tph - 1 - r : r;
+    t.q_row0 = 0;
+    t.kv_row0 = 0;
+    t.sq = p.sq;
+    t.skv = p.skv;
+    t.valid = true;
+    return t;
+  }
+  t.h = lin / tph;
+  int r = lin - t.h * tph;
+  const int32_t* pre = p.tile_prefix;
+  const int total = pre[p.nbatch];
+  t.valid = r < total;
+  if (!t.valid) return t;
+  if (p.reverse_tiles) r = total - 1 - r;
+  // largest b with pre[b] <= r (pre is non-decreasing, pre[0] = 0)
+  int lo = 0, hi = p.nbatch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  t.b = lo;
+  t.qt = r - pre[lo];
+  // clamp so a corrupt cu_seqlens can only shrink the work, never reach outside [0, T)
+  const int q0 = min(max(p.cu_q[lo], 0), p.tq), q1 = min(max(p.cu_q[lo + 1], q0), p.tq);
+  const int k0 = min(max(p.cu_kv[lo], 0), p.tkv), k1 = min(max(p.cu_kv[lo + 1], k0), p.tkv);
+  t.q_row0 = q0;
+  t.kv_row0 = k0;
+  t.sq = q1 - q0;
+  t.skv = k1 - k0;
+  return t;
+}
+
+// Rows of a sequence clamped the same way map_tile clamps them.
+__device__ __forceinline__ int seq_rows(const int32_t* cu, int b, int total) {
+  const int a = min(max(cu[b], 0), total);
+  const int e = min(max(cu[b + 1], a), total);
+  return e - a;
+}
+
+// Key range [lo, hi] any row of [i_first, i_last] may keep (window and length).
+__device__ __forceinline__ void key_range(const Params& p, int i_first, int i_last, int skv, int* lo, int* hi) {
+  int a = 0, e = skv - 1;
+  if (p.band) {
+    a = max(a, i_first - p.pre);
+    e = min(e, i_last + p.next);
+  }
+  *lo = a;
+  *hi = e;
+}
+
+}  // namespace fa

@@ -1,0 +1,69 @@
+// Internal: the parameter block phase 1 fills and the device kernels read.
+// Plain C++ (no HIP types) so the host planner builds with any C++ compiler.
+#pragma once
+
+#include <stdint.h>
+
+namespace fa {
+
+// Which kernel family a plan launches.
+enum KernelKind : int32_t {
+  KERNEL_MFMA = 0,    // bf16/fp16, MFMA 32x32x16, D in {64,128}, Dr in {0,64}, Dv == D
+  KERNEL_GENERIC = 1, // any dtype, one query row per lane, fp32 VALU dot products
+};
+
+// Tile of the MFMA kernel: 4 wavefronts x 32 query rows, 64 keys per step.
+constexpr int kMfmaBM = 128;
+constexpr int kMfmaBN = 64;
+constexpr int kMfmaThreads = 256;
+// Tile of the generic kernel: one wavefront, one query row per lane.
+constexpr int kGenericBM = 64;
+constexpr int kGenericBN = 32;
+constexpr int kGenericThreads = 64;
+
+struct Params {
+  // device addresses
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* qr;        // may be null
+  const void* kr;        // may be null
+  void* o;
+  float* smax;           // may be null
+  float* ssum;           // may be null
+  const uint8_t* mask;   // may be null
+  const float* sink;     // may be null
+  const int32_t* cu_q;   // TND only
+  const int32_t* cu_kv;  // TND only
+  int32_t* tile_prefix;  // TND only: workspace, [nbatch + 1]
+
+  // element strides: batch, row (sequence position / token), head
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t qr_sb, qr_ss, qr_sh;
+  int64_t kr_sb, kr_ss, kr_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t st_sb, st_ss, st_sh;           // statistics (the 8 slots are contiguous)
+  int64_t m_sb, m_sh, m_sq, m_sk;        // mask (0 for broadcast dims)
+  int32_t m_rows, m_cols;                // TND: extent of the 2-D mask
+
+  int32_t nbatch;   // B (dense) or number of sequences (TND)
+  int32_t nq, nkv, group;
+  int32_t sq, skv;  // dense: per-batch lengths; TND: unused (from cu_seqlens)
+  int32_t tq, tkv;  // TND: total rows of q / k
+  int32_t d, dr, dv;
+
+  float scale;       // scale_value
+  float scale_log2;  // scale_value * log2(e)
+  int32_t pre, next; // window bounds (next already min(next,0) under causal), clamped
+  int32_t band;      // window active (mask given or causal)
+  int32_t has_mask, has_sink, varlen;
+  int32_t mask_everywhere;  // read the mask in every block (window cuts nothing)
+
+  int32_t tiles_per_head;   // dense: ceil(sq / BM); TND: ceil(tq / BM) + nbatch (upper bound)
+  int32_t num_wg;           // grid size
+  int32_t reverse_tiles;    // schedule later (heavier) query tiles first
+};
+
+}  // namespace fa

@@ -1,0 +1,402 @@
+// Phase 1 of the two-phase forward: argument validation and planning.
+//
+// Host-only and synchronous: reads tensor descriptors, never device memory.
+// The checks follow the constraint lists of the aclnnFlashAttentionScore page
+// (约束与限制) and the aclnnFlashAttentionVarLenScoreV5 page (约束说明 and the
+// 返回值 error table); the status numbers are the pages' aclnn codes.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "fa_fwd.h"
+#include "fa_params.h"
+#include "fa_plan.h"
+
+namespace {
+
+thread_local char g_err[512] = "no error";
+
+fa_status fail(fa_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+enum Layout { L_BNSD, L_BSND, L_BSH, L_SBH, L_TND, L_BAD };
+
+Layout parse_layout(const char* s) {
+  if (!strcmp(s, "BNSD")) return L_BNSD;
+  if (!strcmp(s, "BSND")) return L_BSND;
+  if (!strcmp(s, "BSH")) return L_BSH;
+  if (!strcmp(s, "SBH")) return L_SBH;
+  if (!strcmp(s, "TND")) return L_TND;
+  return L_BAD;
+}
+
+const char* dtype_name(int32_t dt) {
+  switch (dt) {
+    case FA_DTYPE_F32: return "f32";
+    case FA_DTYPE_F16: return "f16";
+    case FA_DTYPE_BF16: return "bf16";
+    case FA_DTYPE_U8: return "u8";
+    case FA_DTYPE_BOOL: return "bool";
+    case FA_DTYPE_I32: return "i32";
+    case FA_DTYPE_I64: return "i64";
+  }
+  return "?";
+}
+
+// A q/k/v-like tensor seen through its layout.
+struct View {
+  int64_t b, s, n, d;     // batch, rows, heads, head dim (TND: b = 1, s = T)
+  int64_t sb, ss, sh;     // element strides
+};
+
+// Decode `t` in layout L.  For BSH/SBH the hidden size H is split by either a
+// known head count (heads > 0) or a known head dim (hdim > 0).
+fa_status decode(const fa_tensor* t, Layout L, const char* name, int64_t heads, int64_t hdim, View* v) {
+  const int want = (L == L_BNSD || L == L_BSND) ? 4 : 3;
+  if (t->ndim != want)
+    return fail(FA_ERR_PARAM_INVALID, "%s: %d dims, layout needs %d", name, t->ndim, want);
+  for (int i = 0; i < want; ++i)
+    if (t->shape[i] < 0) return fail(FA_ERR_PARAM_INVALID, "%s: negative extent in dim %d", name, i);
+  if (t->stride[want - 1] != 1 && t->shape[want - 1] > 1)
+    return fail(FA_ERR_PARAM_INVALID, "%s: last dimension must be contiguous (stride 1)", name);
+  switch (L) {
+    case L_BNSD:
+      *v = {t->shape[0], t->shape[2], t->shape[1], t->shape[3], t->stride[0], t->stride[2], t->stride[1]};
+      return FA_OK;
+    case L_BSND:
+      *v = {t->shape[0], t->shape[1], t->shape[2], t->shape[3], t->stride[0], t->stride[1], t->stride[2]};
+      return FA_OK;
+    case L_TND:
+      *v = {1, t->shape[0], t->shape[1], t->shape[2], 0, t->stride[0], t->stride[1]};
+      return FA_OK;
+    case L_BSH:
+    case L_SBH: {
+      const int64_t H = t->shape[2];
+      int64_t n, d;
+      if (heads > 0) {
+        if (H % heads) return fail(FA_ERR_UNSUPPORTED, "%s: H=%lld not divisible by %lld heads", name, (long long)H, (long long)heads);
+        n = heads;
+        d = H / heads;
+      } else {
+        if (hdim <= 0 || H % hdim)
+          return fail(FA_ERR_UNSUPPORTED, "%s: H=%lld not a multiple of head dim %lld", name, (long long)H, (long long)hdim);
+        d = hdim;
+        n = H / hdim;
+      }
+      if (L == L_BSH)
+        *v = {t->shape[0], t->shape[1], n, d, t->stride[0], t->stride[1], d};
+      else
+        *v = {t->shape[1], t->shape[0], n, d, t->stride[1], t->stride[0], d};
+      return FA_OK;
+    }
+    default:
+      return fail(FA_ERR_PARAM_INVALID, "bad layout");
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool vec_ok(const void* p, const View& v) {
+  // 16-byte vector access of 16-bit elements at every row start
+  return aligned16(p) && (v.sb % 8 == 0) && (v.ss % 8 == 0) && (v.sh % 8 == 0);
+}
+
+// Window bounds are clamped to +-2^28, which is "unbounded" for sequences of
+// at most 2^24 rows and keeps every row +- bound sum inside int32 on the device.
+int64_t clamp_window(int64_t x) {
+  const int64_t lim = (int64_t)1 << 28;
+  return x < -lim ? -lim : (x > lim ? lim : x);
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" const char* fa_last_error_message(void) { return g_err; }
+
+void fa_set_error(const char* msg) { snprintf(g_err, sizeof(g_err), "%s", msg); }
+
+extern "C" void fa_plan_destroy(fa_plan* plan) { delete plan; }
+
+extern "C" int32_t fa_plan_describe(const fa_plan* plan, char* buf, size_t len) {
+  if (!plan || !buf) return -1;
+  const fa::Params& p = plan->p;
+  const int n = snprintf(buf, len,
+                         "kernel=%s dtype=%s d=%d dr=%d dv=%d bm=%d bn=%d grid=%d block=%d ws=%llu "
+                         "varlen=%d band=%d pre=%d next=%d mask=%d mask_everywhere=%d sink=%d "
+                         "nq=%d nkv=%d tiles_per_head=%d reverse=%d",
+                         plan->kind == fa::KERNEL_MFMA ? "mfma" : "generic", dtype_name(plan->dtype), p.d, p.dr,
+                         p.dv, plan->bm, plan->bn, p.num_wg, plan->block, (unsigned long long)plan->ws_bytes,
+                         p.varlen, p.band, p.pre, p.next, p.has_mask, p.mask_everywhere, p.has_sink, p.nq, p.nkv,
+                         p.tiles_per_head, p.reverse_tiles);
+  return n;
+}
+
+extern "C" fa_status fa_fwd_get_workspace_size(
+    const fa_tensor* query, const fa_tensor* query_rope, const fa_tensor* key, const fa_tensor* key_rope,
+    const fa_tensor* value, const fa_tensor* real_shift, const fa_tensor* atten_mask, const fa_tensor* sink,
+    const fa_tensor* cu_seqlens_q, const fa_tensor* cu_seqlens_kv, double scale_value, double keep_prob,
+    int64_t pre_tokens, int64_t next_tokens, int64_t head_num, const char* input_layout, int64_t inner_precise,
+    int64_t sparse_mode, int32_t causal, const char* softmax_out_layout, const fa_tensor* softmax_max,
+    const fa_tensor* softmax_sum, const fa_tensor* attention_out, uint64_t* workspace_size, fa_plan** plan) {
+  if (plan) *plan = nullptr;
+  // ---- required pointers (161001)
+  if (!query) return fail(FA_ERR_PARAM_NULLPTR, "query is NULL");
+  if (!key) return fail(FA_ERR_PARAM_NULLPTR, "key is NULL");
+  if (!value) return fail(FA_ERR_PARAM_NULLPTR, "value is NULL");
+  if (!attention_out) return fail(FA_ERR_PARAM_NULLPTR, "attention_out is NULL");
+  if (!input_layout) return fail(FA_ERR_PARAM_NULLPTR, "input_layout is NULL");
+  if (!workspace_size) return fail(FA_ERR_PARAM_NULLPTR, "workspace_size is NULL");
+  if (!plan) return fail(FA_ERR_PARAM_NULLPTR, "plan is NULL");
+  if ((query_rope == nullptr) != (key_rope == nullptr))
+    return fail(FA_ERR_PARAM_NULLPTR, "query_rope and key_rope must be given together");
+
+  // ---- dtypes and formats (161002)
+  const Layout L = parse_layout(input_layout);
+  if (L == L_BAD) return fail(FA_ERR_PARAM_INVALID, "input_layout '%s' not one of BNSD BSND BSH SBH TND", input_layout);
+  const int32_t dt = query->dtype;
+  if (dt != FA_DTYPE_F32 && dt != FA_DTYPE_F16 && dt != FA_DTYPE_BF16)
+    return fail(FA_ERR_PARAM_INVALID, "query dtype %s not f32/f16/bf16", dtype_name(dt));
+  if (key->dtype != dt || value->dtype != dt)
+    return fail(FA_ERR_PARAM_INVALID, "query/key/value dtypes differ");
+  if (attention_out->dtype != dt) return fail(FA_ERR_PARAM_INVALID, "attention_out dtype must equal query's");
+  if (query_rope) {
+    if (dt == FA_DTYPE_F32) return fail(FA_ERR_PARAM_INVALID, "rope parts need f16/bf16 inputs");
+    if (query_rope->dtype != dt || key_rope->dtype != dt)
+      return fail(FA_ERR_PARAM_INVALID, "rope dtypes must equal query's");
+  }
+  if (atten_mask && atten_mask->dtype != FA_DTYPE_U8 && atten_mask->dtype != FA_DTYPE_BOOL)
+    return fail(FA_ERR_PARAM_INVALID, "atten_mask dtype %s not u8/bool", dtype_name(atten_mask->dtype));
+  if (sink && sink->dtype != FA_DTYPE_F32) return fail(FA_ERR_PARAM_INVALID, "sink dtype must be f32");
+  if (softmax_max && softmax_max->dtype != FA_DTYPE_F32) return fail(FA_ERR_PARAM_INVALID, "softmax_max must be f32");
+  if (softmax_sum && softmax_sum->dtype != FA_DTYPE_F32) return fail(FA_ERR_PARAM_INVALID, "softmax_sum must be f32");
+  const char* sol = softmax_out_layout ? softmax_out_layout : "";
+  const bool stats_same_as_input = !strcmp(sol, "same_as_input");
+  if (!stats_same_as_input && sol[0] != '\0')
+    return fail(FA_ERR_PARAM_INVALID, "softmax_out_layout '%s' not \"\" or \"same_as_input\"", sol);
+  if (L == L_TND) {
+    if (!cu_seqlens_q || !cu_seqlens_kv) return fail(FA_ERR_PARAM_NULLPTR, "TND needs cu_seqlens_q and cu_seqlens_kv");
+    if (cu_seqlens_q->dtype != FA_DTYPE_I32 || cu_seqlens_kv->dtype != FA_DTYPE_I32)
+      return fail(FA_ERR_PARAM_INVALID, "cu_seqlens must be i32");
+    if (cu_seqlens_q->ndim != 1 || cu_seqlens_kv->ndim != 1)
+      return fail(FA_ERR_PARAM_INVALID, "cu_seqlens must be 1-D");
+  }
+
+  // ---- attributes (561103)
+  if (real_shift) return fail(FA_ERR_UNSUPPORTED, "real_shift (pse) is not supported");
+  if (keep_prob != 1.0) return fail(FA_ERR_UNSUPPORTED, "keep_prob must be 1 (no dropout)");
+  if (sparse_mode != 0) return fail(FA_ERR_UNSUPPORTED, "sparse_mode %lld unsupported (only 0)", (long long)sparse_mode);
+  if (inner_precise < 0 || inner_precise > 2) return fail(FA_ERR_UNSUPPORTED, "inner_precise must be 0, 1 or 2");
+  if (!isfinite(scale_value) || scale_value < 0.0) return fail(FA_ERR_UNSUPPORTED, "scale_value must be finite and >= 0");
+  if (head_num <= 0 || head_num > 256) return fail(FA_ERR_UNSUPPORTED, "head_num %lld outside 1..256", (long long)head_num);
+  if (L != L_TND && (cu_seqlens_q || cu_seqlens_kv))
+    return fail(FA_ERR_UNSUPPORTED, "cu_seqlens only apply to TND");
+
+  // ---- shapes
+  fa_status st;
+  View q, k, v, o, qr{}, kr{};
+  if ((st = decode(query, L, "query", head_num, 0, &q))) return st;
+  if (q.n != head_num) return fail(FA_ERR_UNSUPPORTED, "head_num %lld != query heads %lld", (long long)head_num, (long long)q.n);
+  if ((st = decode(key, L, "key", 0, q.d, &k))) return st;
+  if (L == L_BSH || L == L_SBH) {
+    if ((st = decode(value, L, "value", k.n, 0, &v))) return st;
+    if ((st = decode(attention_out, L, "attention_out", q.n, 0, &o))) return st;
+  } else {
+    if ((st = decode(value, L, "value", 0, 0, &v))) return st;
+    if ((st = decode(attention_out, L, "attention_out", 0, 0, &o))) return st;
+  }
+  if (q.d != k.d) return fail(FA_ERR_UNSUPPORTED, "query D %lld != key D %lld", (long long)q.d, (long long)k.d);
+  if (v.d > k.d) return fail(FA_ERR_UNSUPPORTED, "value D %lld > key D %lld", (long long)v.d, (long long)k.d);
+  if (q.d < 1 || v.d < 1) return fail(FA_ERR_UNSUPPORTED, "head dim must be >= 1");
+  if (k.n < 1 || q.n % k.n) return fail(FA_ERR_UNSUPPORTED, "Nq %lld not a multiple of Nkv %lld", (long long)q.n, (long long)k.n);
+  if (v.n != k.n) return fail(FA_ERR_UNSUPPORTED, "value heads %lld != key heads %lld", (long long)v.n, (long long)k.n);
+  if (L != L_TND && (q.b != k.b || q.b != v.b)) return fail(FA_ERR_UNSUPPORTED, "batch sizes of q/k/v differ");
+  if (k.s != v.s) return fail(FA_ERR_UNSUPPORTED, "key rows %lld != value rows %lld", (long long)k.s, (long long)v.s);
+  if (o.b != q.b || o.s != q.s || o.n != q.n || o.d != v.d)
+    return fail(FA_ERR_UNSUPPORTED, "attention_out shape must be query's with last dim Dv");
+  int64_t dr = 0;
+  if (query_rope) {
+    if ((st = decode(query_rope, L, "query_rope", q.n, 0, &qr))) return st;
+    if ((st = decode(key_rope, L, "key_rope", k.n, 0, &kr))) return st;
+    if (qr.b != q.b || qr.s != q.s || qr.n != q.n) return fail(FA_ERR_UNSUPPORTED, "query_rope shape must match query's");
+    if (kr.b != k.b || kr.s != k.s || kr.n != k.n) return fail(FA_ERR_UNSUPPORTED, "key_rope shape must match key's");
+    if (qr.d != kr.d || qr.d < 1) return fail(FA_ERR_UNSUPPORTED, "rope head dims differ");
+    dr = qr.d;
+  }
+  if (q.d + dr > 256 || v.d > 256)
+    return fail(FA_ERR_UNSUPPORTED, "head dim D+Dr=%lld or Dv=%lld above 256", (long long)(q.d + dr), (long long)v.d);
+  if (q.s > (1 << 24) || k.s > (1 << 24)) return fail(FA_ERR_UNSUPPORTED, "more than 2^24 rows");
+
+  int64_t nbatch = q.b;
+  if (L == L_TND) {
+    nbatch = cu_seqlens_q->shape[0] - 1;
+    if (nbatch < 1 || cu_seqlens_kv->shape[0] != cu_seqlens_q->shape[0])
+      return fail(FA_ERR_UNSUPPORTED, "cu_seqlens need B+1 >= 2 entries, equal for q and kv");
+    if (nbatch > 20000) return fail(FA_ERR_UNSUPPORTED, "more than 20000 sequences");
+    if (!cu_seqlens_q->data || !cu_seqlens_kv->data) return fail(FA_ERR_PARAM_NULLPTR, "cu_seqlens data is NULL");
+  }
+
+  if (atten_mask) {
+    const fa_tensor* m = atten_mask;
+    if (L == L_TND) {
+      if (m->ndim != 2) return fail(FA_ERR_UNSUPPORTED, "TND takes a 2-D atten_mask");
+    } else if (m->ndim == 4) {
+      if (!((m->shape[0] == q.b || m->shape[0] == 1) && (m->shape[1] == q.n || m->shape[1] == 1) &&
+            m->shape[2] == q.s && m->shape[3] == k.s))
+        return fail(FA_ERR_UNSUPPORTED, "atten_mask shape must be [B|1, N|1, Sq, Skv]");
+      if (m->shape[1] == 1 && m->shape[0] != 1 && m->shape[0] != q.b)
+        return fail(FA_ERR_UNSUPPORTED, "atten_mask shape must be [B|1, N|1, Sq, Skv]");
+    } else if (m->ndim == 2) {
+      if (m->shape[0] != q.s || m->shape[1] != k.s) return fail(FA_ERR_UNSUPPORTED, "atten_mask shape must be [Sq, Skv]");
+    } else {
+      return fail(FA_ERR_UNSUPPORTED, "atten_mask must be 2-D or 4-D");
+    }
+    if (!m->data && m->shape[0] * m->shape[1] > 0) return fail(FA_ERR_PARAM_NULLPTR, "atten_mask data is NULL");
+  }
+  if (sink) {
+    if (sink->ndim != 1 || sink->shape[0] != q.n) return fail(FA_ERR_UNSUPPORTED, "sink must be [Nq]");
+    if (!sink->data) return fail(FA_ERR_PARAM_NULLPTR, "sink data is NULL");
+  }
+  const fa_tensor* stats[2] = {softmax_max, softmax_sum};
+  int64_t st_sb = 0, st_ss = 0, st_sh = 0;
+  for (int i = 0; i < 2; ++i) {
+    const fa_tensor* s = stats[i];
+    if (!s) continue;
+    const char* nm = i ? "softmax_sum" : "softmax_max";
+    int64_t sb, ss, sh;
+    if (L == L_TND) {
+      if (s->ndim != 3 || s->shape[2] != 8) return fail(FA_ERR_UNSUPPORTED, "%s must be [N,T,8] or [T,N,8]", nm);
+      if (stats_same_as_input) {
+        if (s->shape[0] != q.s || s->shape[1] != q.n) return fail(FA_ERR_UNSUPPORTED, "%s must be [T,N,8]", nm);
+        sb = 0; ss = s->stride[0]; sh = s->stride[1];
+      } else {
+        if (s->shape[0] != q.n || s->shape[1] != q.s) return fail(FA_ERR_UNSUPPORTED, "%s must be [N,T,8]", nm);
+        sb = 0; sh = s->stride[0]; ss = s->stride[1];
+      }
+    } else {
+      if (s->ndim != 4 || s->shape[0] != q.b || s->shape[1] != q.n || s->shape[2] != q.s || s->shape[3] != 8)
+        return fail(FA_ERR_UNSUPPORTED, "%s must be [B,N,Sq,8]", nm);
+      sb = s->stride[0]; sh = s->stride[1]; ss = s->stride[2];
+    }
+    if (s->stride[s->ndim - 1] != 1) return fail(FA_ERR_PARAM_INVALID, "%s: last dimension must be contiguous", nm);
+    if (i == 0) {
+      st_sb = sb; st_ss = ss; st_sh = sh;
+    } else if (softmax_max && (sb != st_sb || ss != st_ss || sh != st_sh)) {
+      return fail(FA_ERR_UNSUPPORTED, "softmax_max and softmax_sum must have equal strides");
+    } else {
+      st_sb = sb; st_ss = ss; st_sh = sh;
+    }
+  }
+
+  // ---- window
+  const bool band = atten_mask != nullptr || causal != 0;
+  int64_t pre = clamp_window(pre_tokens), nxt = clamp_window(next_tokens);
+  if (causal && nxt > 0) nxt = 0;
+  if (band && pre + nxt < 0)
+    return fail(FA_ERR_UNSUPPORTED, "preTokens + nextTokens < 0: the window is empty");
+
+  // ---- kernel choice
+  fa_plan* pl = new (std::nothrow) fa_plan();
+  if (!pl) return fail(FA_ERR_UNSUPPORTED, "out of host memory");
+  fa::Params& p = pl->p;
+  pl->dtype = dt;
+  const bool stats_vec = (!softmax_max || aligned16(softmax_max->data)) && (!softmax_sum || aligned16(softmax_sum->data)) &&
+                         st_sb % 4 == 0 && st_ss % 4 == 0 && st_sh % 4 == 0;
+  const bool mfma_ok = (dt == FA_DTYPE_F16 || dt == FA_DTYPE_BF16) && (q.d == 64 || q.d == 128) && v.d == q.d &&
+                       (dr == 0 || dr == 64) && vec_ok(query->data, q) && vec_ok(key->data, k) &&
+                       vec_ok(value->data, v) && vec_ok(attention_out->data, o) &&
+                       (!query_rope || (vec_ok(query_rope->data, qr) && vec_ok(key_rope->data, kr))) && stats_vec;
+  pl->kind = mfma_ok ? fa::KERNEL_MFMA : fa::KERNEL_GENERIC;
+  pl->bm = mfma_ok ? fa::kMfmaBM : fa::kGenericBM;
+  pl->bn = mfma_ok ? fa::kMfmaBN : fa::kGenericBN;
+  pl->block = mfma_ok ? fa::kMfmaThreads : fa::kGenericThreads;
+
+  p.q = query->data; p.k = key->data; p.v = value->data;
+  p.qr = query_rope ? query_rope->data : nullptr;
+  p.kr = key_rope ? key_rope->data : nullptr;
+  p.o = attention_out->data;
+  p.smax = softmax_max ? static_cast<float*>(softmax_max->data) : nullptr;
+  p.ssum = softmax_sum ? static_cast<float*>(softmax_sum->data) : nullptr;
+  p.mask = atten_mask ? static_cast<const uint8_t*>(atten_mask->data) : nullptr;
+  p.sink = sink ? static_cast<const float*>(sink->data) : nullptr;
+  p.cu_q = L == L_TND ? static_cast<const int32_t*>(cu_seqlens_q->data) : nullptr;
+  p.cu_kv = L == L_TND ? static_cast<const int32_t*>(cu_seqlens_kv->data) : nullptr;
+  p.tile_prefix = nullptr;  // set from the workspace in phase 2
+  p.q_sb = q.sb; p.q_ss = q.ss; p.q_sh = q.sh;
+  p.k_sb = k.sb; p.k_ss = k.ss; p.k_sh = k.sh;
+  p.v_sb = v.sb; p.v_ss = v.ss; p.v_sh = v.sh;
+  p.qr_sb = qr.sb; p.qr_ss = qr.ss; p.qr_sh = qr.sh;
+  p.kr_sb = kr.sb; p.kr_ss = kr.ss; p.kr_sh = kr.sh;
+  p.o_sb = o.sb; p.o_ss = o.ss; p.o_sh = o.sh;
+  p.st_sb = st_sb; p.st_ss = st_ss; p.st_sh = st_sh;
+  p.m_sb = p.m_sh = p.m_sq = p.m_sk = 0;
+  p.m_rows = p.m_cols = 0;
+  if (atten_mask) {
+    const fa_tensor* m = atten_mask;
+    if (m->ndim == 4) {
+      p.m_sb = m->shape[0] > 1 ? m->stride[0] : 0;
+      p.m_sh = m->shape[1] > 1 ? m->stride[1] : 0;
+      p.m_sq = m->stride[2];
+      p.m_sk = m->stride[3];
+    } else {
+      p.m_sq = m->stride[0];
+      p.m_sk = m->stride[1];
+      p.m_rows = (int32_t)(m->shape[0] < (1 << 24) ? m->shape[0] : (1 << 24));
+      p.m_cols = (int32_t)(m->shape[1] < (1 << 24) ? m->shape[1] : (1 << 24));
+    }
+  }
+  p.nbatch = (int32_t)nbatch;
+  p.nq = (int32_t)q.n;
+  p.nkv = (int32_t)k.n;
+  p.group = (int32_t)(q.n / k.n);
+  p.varlen = L == L_TND;
+  p.sq = p.varlen ? 0 : (int32_t)q.s;
+  p.skv = p.varlen ? 0 : (int32_t)k.s;
+  p.tq = p.varlen ? (int32_t)q.s : 0;
+  p.tkv = p.varlen ? (int32_t)k.s : 0;
+  p.d = (int32_t)q.d;
+  p.dr = (int32_t)dr;
+  p.dv = (int32_t)v.d;
+  p.scale = (float)scale_value;
+  p.scale_log2 = (float)(scale_value * 1.4426950408889634);
+  p.band = band;
+  p.pre = (int32_t)pre;
+  p.next = (int32_t)nxt;
+  p.has_mask = atten_mask != nullptr;
+  p.has_sink = sink != nullptr;
+  // The window cuts nothing when it spans every (row, key) pair: then a given
+  // mask must be read in every block, not just those crossing the window edge.
+  const int64_t max_rows = q.s, max_keys = k.s;  // per-sequence lengths are at most these
+  const bool window_cuts = band && (pre < max_rows - 1 || nxt < max_keys - 1);
+  p.mask_everywhere = p.has_mask && !window_cuts;
+  p.reverse_tiles = band && nxt < max_keys - 1;
+
+  const int64_t bm = pl->bm;
+  int64_t tiles, wg;
+  if (p.varlen) {
+    tiles = cdiv(q.s, bm) + nbatch;
+    wg = q.s > 0 ? tiles * q.n : 0;
+    pl->ws_bytes = (uint64_t)(nbatch + 1) * sizeof(int32_t);
+  } else {
+    tiles = cdiv(q.s, bm);
+    wg = tiles * q.b * q.n;
+    pl->ws_bytes = 0;
+  }
+  if (wg >= ((int64_t)1 << 31)) {
+    delete pl;
+    return fail(FA_ERR_UNSUPPORTED, "grid of %lld workgroups too large", (long long)wg);
+  }
+  p.tiles_per_head = (int32_t)tiles;
+  p.num_wg = (int32_t)wg;
+  *workspace_size = pl->ws_bytes;
+  *plan = pl;
+  return FA_OK;
+}

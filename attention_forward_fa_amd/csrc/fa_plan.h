@@ -1,0 +1,18 @@
+// Internal: the plan object behind the opaque fa_plan handle.
+#pragma once
+
+#include <stdint.h>
+
+#include "fa_params.h"
+
+struct fa_plan {
+  fa::Params p;        // kernel parameter block (tile_prefix filled in phase 2)
+  int32_t kind;        // fa::KernelKind
+  int32_t dtype;       // fa_dtype of q/k/v/o
+  int32_t bm, bn;      // query rows and keys per tile step
+  int32_t block;       // threads per workgroup
+  uint64_t ws_bytes;   // device workspace phase 2 needs
+};
+
+// Record the message fa_last_error_message() returns on this thread.
+void fa_set_error(const char* msg);

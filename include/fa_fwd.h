@@ -1,0 +1,182 @@
+/*
+ * fa_fwd.h -- FlashAttention forward on MI355X (gfx950): the C ABI.
+ *
+ * Computes, per (batch or sequence, query head), the attention forward of the
+ * aclnnFlashAttentionVarLenScoreV5 page (功能说明 -> 计算公式):
+ *
+ *     Attention = Softmax( Mask( scale * (Q K^T + Qrope Krope^T) ), atten_mask ) * V
+ *
+ * with the optional per-head sink logit of the same section (m = max(sink,
+ * max S); the denominator gains e^(sink - m)), and writes the per-row
+ * softmax statistics softmaxMax = m and softmaxSum = l beside the output
+ * (V5 parameter table, rows softmaxMaxOut / softmaxSumOut).
+ *
+ * The call is two-phase, as on both Ascend pages (aclnnFlashAttentionScore
+ * page, 接口原型; V5 page, 函数原型): phase 1 validates the arguments on the
+ * host and returns the workspace size and a plan; phase 2 enqueues the device
+ * work on a HIP stream.
+ *
+ * Conventions
+ *   - Every pointer inside an fa_tensor is a DEVICE address owned by the
+ *     caller; the library never allocates, frees or reads device memory on the
+ *     host.  Host arguments (descriptors, strings, out-pointers) are read only
+ *     during the call.
+ *   - Strides are in elements.  The last dimension of every tensor must have
+ *     stride 1 except where noted.
+ *   - Errors are returned as status codes; nothing is thrown across the ABI.
+ *     fa_last_error_message() gives a human-readable reason for the last
+ *     non-zero status returned on the calling thread.
+ *   - All entry points are thread-safe; plans are immutable after phase 1.
+ */
+#ifndef FA_FWD_H
+#define FA_FWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of fa_tensor.dtype. */
+typedef enum {
+  FA_DTYPE_F32 = 0,
+  FA_DTYPE_F16 = 1,
+  FA_DTYPE_BF16 = 2,
+  FA_DTYPE_U8 = 3,
+  FA_DTYPE_BOOL = 4, /* one byte per element, 0 / 1 */
+  FA_DTYPE_I32 = 5,
+  FA_DTYPE_I64 = 6
+} fa_dtype;
+
+/* A strided view of device memory (the role of aclTensor on the Ascend pages:
+ * shape, dtype, strides, device address).  ndim is 1..4; shape[i] >= 0;
+ * stride[i] in elements; entries at index >= ndim are ignored. */
+typedef struct {
+  void* data;
+  int32_t dtype; /* fa_dtype */
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t stride[4];
+} fa_tensor;
+
+/* Opaque execution plan (the role of aclOpExecutor). */
+typedef struct fa_plan fa_plan;
+
+typedef int32_t fa_status;
+
+/* Status codes.  The first three carry the numbers of the pages' aclnn
+ * return-code table (V5 page, 返回值: ACLNN_ERR_PARAM_NULLPTR 161001,
+ * ACLNN_ERR_PARAM_INVALID 161002, ACLNN_ERR_INNER_NULLPTR 561103). */
+#define FA_OK 0
+#define FA_ERR_PARAM_NULLPTR 161001 /* a required pointer argument is NULL          */
+#define FA_ERR_PARAM_INVALID 161002 /* dtype, layout string or tensor format invalid */
+#define FA_ERR_UNSUPPORTED 561103   /* shape or attribute outside the supported range */
+#define FA_ERR_WORKSPACE 561201     /* phase 2: workspace NULL or smaller than needed */
+#define FA_ERR_RUNTIME 561202       /* phase 2: HIP launch / runtime error            */
+
+/*
+ * Phase 1: validate, plan, and report the device workspace size.
+ *
+ * Passages: V5 page, 函数原型 and the 参数说明 table (argument list and
+ * meaning); aclnnFlashAttentionScore page, aclnnFlashAttentionScoreGetWorkspaceSize
+ * 参数说明 (dense layouts BSH / SBH / BSND / BNSD); MindIE-SD
+ * attention_forward_varlen page (int32 cu_seqlens with a leading 0, causal).
+ *
+ * Arguments (device tensors unless stated; NULL = absent for optional ones):
+ *   query, key, value   q/k/v, one dtype of F32, F16, BF16.  Layout by
+ *                       input_layout: BNSD [B,N,S,D], BSND [B,S,N,D],
+ *                       BSH [B,S,N*D], SBH [S,B,N*D], TND [T,N,D].
+ *                       Nq % Nkv == 0 (GQA / MQA: query head h reads kv
+ *                       head h / (Nq/Nkv)); D(q) == D(k) >= D(v).
+ *   query_rope, key_rope  optional, both or neither; F16 or BF16 equal to q's
+ *                       dtype, same layout and sizes as query / key with their
+ *                       own last dim Dr.  Adds Qrope Krope^T to the scores.
+ *   real_shift          pse: must be NULL (the additive bias is not built).
+ *   atten_mask          optional U8/BOOL, nonzero = position EXCLUDED.
+ *                       Dense: [B,N,Sq,Skv], [B,1,Sq,Skv], [1,1,Sq,Skv] or
+ *                       [Sq,Skv] (any strides).  TND: a 2-D [S1,S2] matrix
+ *                       read in sequence-local coordinates; positions outside
+ *                       it count as excluded.  The mask is read only in KV
+ *                       blocks that cross the preTokens/nextTokens window
+ *                       boundary or the sequence end (sparse mode 0 requires
+ *                       the mask to agree with the window); when the window
+ *                       cuts nothing it is read everywhere.
+ *   sink                optional F32 [Nq]: per-query-head sink logit, in
+ *                       logit units (not scaled).  -inf equals no sink.
+ *   cu_seqlens_q, cu_seqlens_kv  TND only (required there, NULL otherwise):
+ *                       I32 [B+1], cumulative lengths with a leading 0,
+ *                       non-decreasing, last entry == T of q / k.  Read by the
+ *                       device in phase 2 only; zero-length sequences allowed.
+ *   scale_value         finite, >= 0; multiplies both score terms.
+ *   keep_prob           must be 1.0 (no dropout).
+ *   pre_tokens, next_tokens  window: key j is kept for row i iff
+ *                       -pre <= j - i <= next (inclusive), counted from the
+ *                       start of each sequence.  Active only when atten_mask
+ *                       is given or causal != 0; then pre + next' >= 0 is
+ *                       required, next' = min(next, 0) under causal.
+ *   head_num            Nq; must equal the query's N (splits H for BSH/SBH).
+ *   input_layout        "BNSD" | "BSND" | "BSH" | "SBH" | "TND".
+ *   inner_precise       0, 1 or 2; accepted, numerics are the same for all
+ *                       (fp32 accumulation; rows with no kept key are defined).
+ *   sparse_mode         must be 0.
+ *   causal              nonzero: exclude j > i (top-left aligned).
+ *   softmax_out_layout  NULL or "" or "same_as_input" (TND stats layout).
+ *   softmax_max, softmax_sum  optional F32 outputs (NULL = not written):
+ *                       dense [B,N,Sq,8]; TND [N,T,8] for "" and [T,N,8] for
+ *                       "same_as_input".  All 8 trailing slots hold the same
+ *                       per-row value: m = max(sink, max_j s_ij) in natural-log
+ *                       units and l = sum_j e^(s_ij - m) (+ e^(sink - m)).
+ *                       A row with no kept key gets m = -inf, l = 0 (or
+ *                       m = sink, l = 1 with a finite sink).
+ *   attention_out       output, q's dtype, q's layout with last dim Dv.  Rows
+ *                       with no kept key are 0.  Rounded to nearest even.
+ *   workspace_size      host out: bytes of device workspace phase 2 needs
+ *                       (0 for dense layouts).
+ *   plan                host out: a new plan, to be released with
+ *                       fa_plan_destroy().  It records the tensors' device
+ *                       addresses; it may be executed any number of times.
+ *
+ * Returns FA_OK, FA_ERR_PARAM_NULLPTR, FA_ERR_PARAM_INVALID or
+ * FA_ERR_UNSUPPORTED.  On error *plan is set to NULL.  No device work.
+ */
+fa_status fa_fwd_get_workspace_size(
+    const fa_tensor* query, const fa_tensor* query_rope, const fa_tensor* key,
+    const fa_tensor* key_rope, const fa_tensor* value, const fa_tensor* real_shift,
+    const fa_tensor* atten_mask, const fa_tensor* sink, const fa_tensor* cu_seqlens_q,
+    const fa_tensor* cu_seqlens_kv, double scale_value, double keep_prob, int64_t pre_tokens,
+    int64_t next_tokens, int64_t head_num, const char* input_layout, int64_t inner_precise,
+    int64_t sparse_mode, int32_t causal, const char* softmax_out_layout,
+    const fa_tensor* softmax_max, const fa_tensor* softmax_sum, const fa_tensor* attention_out,
+    uint64_t* workspace_size, fa_plan** plan);
+
+/*
+ * Phase 2: enqueue the forward on `stream` (a hipStream_t; NULL = the null
+ * stream).  Asynchronous: the caller synchronises.  `workspace` is a device
+ * buffer of at least the size phase 1 reported (may be NULL when that size is
+ * 0); the library uses it as scratch and it must not be in use by another
+ * call on an overlapping stream.  Passage: V5 page, the second-phase call
+ * (workspace, workspaceSize, executor, stream).
+ *
+ * Returns FA_OK, FA_ERR_PARAM_NULLPTR (plan NULL), FA_ERR_WORKSPACE or
+ * FA_ERR_RUNTIME.  The plan is not consumed.
+ */
+fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_plan* plan, void* stream);
+
+/* Release a plan from phase 1.  NULL is ignored. */
+void fa_plan_destroy(fa_plan* plan);
+
+/* Text of the chosen kernel, tile and grid, e.g. for logs.  Writes at most
+ * `len` bytes including the terminating NUL into `buf`; returns the length
+ * the full text needs (excluding NUL), or -1 if plan or buf is NULL. */
+int32_t fa_plan_describe(const fa_plan* plan, char* buf, size_t len);
+
+/* Reason for the last non-zero status returned on the calling thread
+ * (static, thread-local storage; never NULL). */
+const char* fa_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_FWD_H */

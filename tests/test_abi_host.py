@@ -1,0 +1,328 @@
+"""The C ABI on the CPU: the library loads, exports what the header declares,
+and phase 1 validates and plans without touching a GPU.
+
+Phase 1 reads only descriptors, so these tests hand it fabricated (aligned,
+never dereferenced) device addresses.  Phase 2 is called only on paths that
+return before any launch (NULL plan, missing workspace).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_forward_fa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_fwd.h")
+
+F32, F16, BF16, U8, BOOL, I32, I64 = range(7)
+ADDR = 0x7F0000000000  # fake, 256-byte aligned
+
+
+def desc(shape, dtype=BF16, strides=None, addr=ADDR):
+    t = _lib.FaTensor()
+    t.data = addr
+    t.dtype = dtype
+    t.ndim = len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for s in reversed(shape):
+            strides.insert(0, acc)
+            acc *= s
+    for i, (s, st) in enumerate(zip(shape, strides)):
+        t.shape[i] = s
+        t.stride[i] = st
+    return t
+
+
+def plan(q, k, v, o, *, qr=None, kr=None, pse=None, mask=None, sink=None, cuq=None, cuk=None, scale=0.088,
+         keep=1.0, pre=2**31 - 1, nxt=2**31 - 1, heads=None, layout=b"BSND", inner=0, sparse=0, causal=0,
+         sol=b"", smax=None, ssum=None):
+    L = _lib.lib()
+    ws = ctypes.c_uint64(123)
+    pl = ctypes.c_void_p(None)
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    if heads is None:
+        axis = {b"BNSD": 1, b"BSND": 2, b"TND": 1}.get(layout)
+        heads = q.shape[axis] if (q is not None and axis is not None) else 24
+    st = L.fa_fwd_get_workspace_size(r(q), r(qr), r(k), r(kr), r(v), r(pse), r(mask), r(sink), r(cuq), r(cuk),
+                                     scale, keep, pre, nxt, heads, layout, inner, sparse, causal, sol, r(smax),
+                                     r(ssum), r(o), ctypes.byref(ws), ctypes.byref(pl))
+    return st, ws.value, pl.value
+
+
+def describe(pl):
+    return _lib.fa_plan_describe(pl)
+
+
+def c2(dtype=BF16):
+    s = [2, 4096, 24, 128]
+    return desc(s, dtype), desc(s, dtype), desc(s, dtype), desc(s, dtype)
+
+
+def test_header_symbols_exported():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:fa_status|void|int32_t|const char\*)\s+(fa_\w+)\s*\(", text, re.M))
+    assert declared == set(_lib.EXPORTED), declared
+    L = _lib.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    for name in ("FA_OK", "FA_ERR_PARAM_NULLPTR", "FA_ERR_PARAM_INVALID", "FA_ERR_UNSUPPORTED",
+                 "FA_ERR_WORKSPACE", "FA_ERR_RUNTIME"):
+        m = re.search(rf"#define {name} (\d+)", text)
+        assert m and int(m.group(1)) == getattr(_lib, name)
+
+
+def test_dense_headline_plan():
+    q, k, v, o = c2()
+    smax = desc([2, 24, 4096, 8], F32)
+    ssum = desc([2, 24, 4096, 8], F32)
+    st, ws, pl = plan(q, k, v, o, smax=smax, ssum=ssum)
+    assert st == 0, _lib.last_error_message()
+    try:
+        assert ws == 0
+        d = describe(pl)
+        assert "kernel=mfma" in d and "grid=1536" in d and "dtype=bf16" in d, d
+    finally:
+        _lib.fa_plan_destroy(pl)
+
+
+def test_varlen_plan_workspace():
+    T, N = 8192, 24
+    q = desc([T, N, 128])
+    cu = desc([17], I32)
+    smax = desc([N, T, 8], F32)
+    st, ws, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND", causal=1, smax=smax, ssum=smax)
+    assert st == 0, _lib.last_error_message()
+    assert ws == 4 * 17
+    d = describe(pl)
+    assert "varlen=1" in d and "grid=1920" in d and "reverse=1" in d, d  # (64 + 16) tiles x 24 heads
+    _lib.fa_plan_destroy(pl)
+
+
+def test_fp32_uses_generic_kernel():
+    s = [1, 2, 128, 64]
+    st, ws, pl = plan(desc(s, F32), desc(s, F32), desc(s, F32), desc(s, F32), layout=b"BNSD")
+    assert st == 0
+    assert "kernel=generic" in describe(pl)
+    _lib.fa_plan_destroy(pl)
+
+
+def test_misaligned_falls_back_to_generic():
+    q, k, v, o = c2()
+    q.data = ADDR + 2
+    st, ws, pl = plan(q, k, v, o)
+    assert st == 0 and "kernel=generic" in describe(pl)
+    _lib.fa_plan_destroy(pl)
+
+
+def test_bsh_sbh_and_gqa_plan():
+    q = desc([2, 100, 8 * 64])
+    k = desc([2, 100, 2 * 64])
+    st, ws, pl = plan(q, k, k, q, layout=b"BSH", heads=8)
+    assert st == 0, _lib.last_error_message()
+    d = describe(pl)
+    assert "nq=8 nkv=2" in d and "d=64" in d
+    _lib.fa_plan_destroy(pl)
+    qs = desc([100, 2, 8 * 64])
+    ks = desc([100, 2, 2 * 64])
+    st, ws, pl = plan(qs, ks, ks, qs, layout=b"SBH", heads=8)
+    assert st == 0
+    _lib.fa_plan_destroy(pl)
+
+
+@pytest.mark.parametrize("which", ["query", "key", "value", "out"])
+def test_null_required_tensor(which):
+    q, k, v, o = c2()
+    args = dict(q=q, k=k, v=v, o=o)
+    args[{"query": "q", "key": "k", "value": "v", "out": "o"}[which]] = None
+    st, ws, pl = plan(args["q"], args["k"], args["v"], args["o"])
+    assert st == 161001 and pl is None
+    assert which in _lib.last_error_message() or "NULL" in _lib.last_error_message()
+
+
+def test_null_layout_and_outputs():
+    q, k, v, o = c2()
+    L = _lib.lib()
+    ws = ctypes.c_uint64(0)
+    pl = ctypes.c_void_p(None)
+    r = ctypes.byref
+    st = L.fa_fwd_get_workspace_size(r(q), None, r(k), None, r(v), None, None, None, None, None, 0.1, 1.0, 0, 0,
+                                     24, None, 0, 0, 0, b"", None, None, r(o), r(ws), r(pl))
+    assert st == 161001
+    st = L.fa_fwd_get_workspace_size(r(q), None, r(k), None, r(v), None, None, None, None, None, 0.1, 1.0, 0, 0,
+                                     24, b"BSND", 0, 0, 0, b"", None, None, r(o), None, r(pl))
+    assert st == 161001
+
+
+def test_rope_pairing():
+    q, k, v, o = c2()
+    st, _, _ = plan(q, k, v, o, qr=desc([2, 4096, 24, 64]))
+    assert st == 161001
+
+
+@pytest.mark.parametrize("case", ["layout", "dtype_mismatch", "out_dtype", "int_q", "rope_f32", "rope_dtype",
+                                  "mask_dtype", "sink_dtype", "stats_dtype", "sol", "ndim", "cu_dtype"])
+def test_invalid_formats(case):
+    q, k, v, o = c2()
+    kw = {}
+    if case == "layout":
+        kw["layout"] = b"NSD"
+    elif case == "dtype_mismatch":
+        k = desc([2, 4096, 24, 128], F16)
+    elif case == "out_dtype":
+        o = desc([2, 4096, 24, 128], F32)
+    elif case == "int_q":
+        q = desc([2, 4096, 24, 128], I32)
+    elif case == "rope_f32":
+        q, k, v, o = c2(F32)
+        kw.update(qr=desc([2, 4096, 24, 64], F32), kr=desc([2, 4096, 24, 64], F32))
+    elif case == "rope_dtype":
+        kw.update(qr=desc([2, 4096, 24, 64], F16), kr=desc([2, 4096, 24, 64], F16))
+    elif case == "mask_dtype":
+        kw["mask"] = desc([4096, 4096], F16)
+    elif case == "sink_dtype":
+        kw["sink"] = desc([24], BF16)
+    elif case == "stats_dtype":
+        kw["smax"] = desc([2, 24, 4096, 8], F16)
+    elif case == "sol":
+        kw["sol"] = b"NTD"
+    elif case == "ndim":
+        q = desc([2, 4096, 24 * 128])
+        kw["heads"] = 24
+    elif case == "cu_dtype":
+        q = desc([100, 24, 128])
+        kw.update(layout=b"TND", cuq=desc([3], I64), cuk=desc([3], I64))
+        k = v = o = q
+    st, _, pl = plan(q, k, v, o, **kw)
+    assert st == 161002, (case, st, _lib.last_error_message())
+    assert pl is None
+
+
+@pytest.mark.parametrize("case", ["keep_prob", "sparse", "pse", "inner", "scale_neg", "scale_nan", "heads",
+                                  "gqa_ratio", "d_mismatch", "dv_gt_d", "batch", "kv_rows", "out_shape",
+                                  "mask_shape", "sink_shape", "stats_shape", "window_empty", "cu_dense",
+                                  "tnd_mask_4d", "big_d", "cu_len"])
+def test_unsupported(case):
+    q, k, v, o = c2()
+    kw = {}
+    if case == "keep_prob":
+        kw["keep"] = 0.9
+    elif case == "sparse":
+        kw["sparse"] = 2
+    elif case == "pse":
+        kw["pse"] = desc([2, 24, 4096, 4096])
+    elif case == "inner":
+        kw["inner"] = 3
+    elif case == "scale_neg":
+        kw["scale"] = -0.1
+    elif case == "scale_nan":
+        kw["scale"] = float("nan")
+    elif case == "heads":
+        kw["heads"] = 12
+    elif case == "gqa_ratio":
+        k = desc([2, 4096, 5, 128])
+        v = desc([2, 4096, 5, 128])
+    elif case == "d_mismatch":
+        k = desc([2, 4096, 24, 64])
+    elif case == "dv_gt_d":
+        v = desc([2, 4096, 24, 256])
+    elif case == "batch":
+        k = desc([3, 4096, 24, 128])
+    elif case == "kv_rows":
+        v = desc([2, 4000, 24, 128])
+    elif case == "out_shape":
+        o = desc([2, 4096, 24, 64])
+    elif case == "mask_shape":
+        kw["mask"] = desc([4096, 4000], U8)
+    elif case == "sink_shape":
+        kw["sink"] = desc([23], F32)
+    elif case == "stats_shape":
+        kw["smax"] = desc([2, 24, 4096, 4], F32)
+    elif case == "window_empty":
+        kw.update(mask=desc([4096, 4096], U8), pre=-5, nxt=2)
+    elif case == "cu_dense":
+        kw.update(cuq=desc([3], I32), cuk=desc([3], I32))
+    elif case == "tnd_mask_4d":
+        q = desc([100, 24, 128])
+        k = v = o = q
+        kw.update(layout=b"TND", cuq=desc([3], I32), cuk=desc([3], I32), mask=desc([1, 1, 100, 100], U8))
+    elif case == "big_d":
+        q, k, v, o = (desc([2, 64, 24, 320]) for _ in range(4))
+    elif case == "cu_len":
+        q = desc([100, 24, 128])
+        k = v = o = q
+        kw.update(layout=b"TND", cuq=desc([3], I32), cuk=desc([4], I32))
+    st, _, pl = plan(q, k, v, o, **kw)
+    assert st == 561103, (case, st, _lib.last_error_message())
+    assert pl is None
+
+
+def test_tnd_requires_cu_seqlens():
+    q = desc([100, 24, 128])
+    st, _, _ = plan(q, q, q, q, layout=b"TND")
+    assert st == 161001
+
+
+def test_window_with_causal_needs_pre_plus_min_next_nonnegative():
+    q, k, v, o = c2()
+    # causal caps next at 0: pre = -1 leaves no key for any row
+    st, _, _ = plan(q, k, v, o, causal=1, pre=-1, nxt=5)
+    assert st == 561103
+    st, _, pl = plan(q, k, v, o, causal=1, pre=0, nxt=5)
+    assert st == 0
+    assert "next=0" in describe(pl)
+    _lib.fa_plan_destroy(pl)
+
+
+def test_band_ignored_without_mask_or_causal():
+    q, k, v, o = c2()
+    st, _, pl = plan(q, k, v, o, pre=-5, nxt=2)  # would be empty, but no mask and no causal -> inactive
+    assert st == 0 and "band=0" in describe(pl)
+    _lib.fa_plan_destroy(pl)
+
+
+def test_mask_everywhere_only_when_window_cuts_nothing():
+    q, k, v, o = c2()
+    m = desc([4096, 4096], U8)
+    st, _, pl = plan(q, k, v, o, mask=m)
+    assert "mask_everywhere=1" in describe(pl)
+    _lib.fa_plan_destroy(pl)
+    st, _, pl = plan(q, k, v, o, mask=m, nxt=0)
+    assert "mask_everywhere=0" in describe(pl)
+    _lib.fa_plan_destroy(pl)
+
+
+def test_phase2_argument_errors_without_launch():
+    L = _lib.lib()
+    assert L.fa_fwd(None, 0, None, None) == 161001
+    T, N = 1000, 4
+    q = desc([T, N, 128])
+    cu = desc([5], I32)
+    st, ws, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND")
+    assert st == 0 and ws == 20
+    assert L.fa_fwd(None, 0, pl, None) == 561201
+    assert L.fa_fwd(ctypes.c_void_p(ADDR), 19, pl, None) == 561201
+    assert "workspace" in _lib.last_error_message()
+    _lib.fa_plan_destroy(pl)
+
+
+def test_plan_destroy_null_and_describe_null():
+    L = _lib.lib()
+    L.fa_plan_destroy(None)
+    assert L.fa_plan_describe(None, None, 0) == -1
+
+
+def test_describe_truncates_safely():
+    q, k, v, o = c2()
+    st, _, pl = plan(q, k, v, o)
+    L = _lib.lib()
+    buf = ctypes.create_string_buffer(8)
+    n = L.fa_plan_describe(pl, buf, 8)
+    assert n > 8 and len(buf.value) == 7
+    _lib.fa_plan_destroy(pl)

@@ -1,0 +1,268 @@
+"""HIP forward vs the CPU oracle, element by element (needs an MI355X).
+
+Small cases cover several tiles, ragged tails and every feature; the
+full-size workloads are compared on sampled rows the oracle computes one by
+one.  Tolerances are the ones stated in ``parity_util``.
+"""
+import math
+
+import pytest
+import torch
+
+import synth
+from attention_forward_fa_amd import _lib, api
+from oracle import attention as orc
+
+from . import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+U = synth.UNBOUNDED
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.lib()  # the HIP library must be built; fails loudly otherwise
+    yield
+
+
+def _report(name, errs):
+    print(f"[parity] {name}: " + " ".join(f"{k}={v:.3g}" for k, v in errs.items()), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# small cases, full comparison
+# ---------------------------------------------------------------------------
+
+SMALL = {
+    "c1_fp32_bnsd": lambda: synth.workload("c1_fp32_bnsd"),
+    "c2_small_bf16": lambda: synth.workload("c2_dense_bsnd", "bf16", small=True),
+    "c2_small_fp16": lambda: synth.workload("c2_dense_bsnd", "fp16", small=True),
+    "c3_small_causal": lambda: synth.workload("c3_causal", small=True),
+    "c3_small_band": lambda: synth.workload("c3_band", small=True),
+    "c4_small_varlen": lambda: synth.workload("c4_varlen_causal", small=True),
+    "c5_small_sink_rope": lambda: synth.workload("c5_varlen_sink_rope", small=True),
+    "bnsd_ragged_201": lambda: synth.dense_case("x", "BNSD", 2, 2, 201, 128, "bf16", 31),
+    "bsnd_d64": lambda: synth.dense_case("x", "BSND", 1, 3, 190, 64, "bf16", 32),
+    "bsnd_d64_rope": lambda: synth.dense_case("x", "BSND", 1, 2, 150, 64, "bf16", 33, drope=64, causal=True),
+    "fp16_rope_sink": lambda: synth.dense_case("x", "BNSD", 1, 2, 260, 128, "fp16", 34, drope=64, sink=True),
+    "gqa_4_2": lambda: synth.dense_case("x", "BNSD", 2, 4, 140, 128, "bf16", 35, nkv=2, causal=True),
+    "mqa_varlen": lambda: synth.varlen_case("x", [70, 0, 129, 1], 4, 128, "bf16", 36, nkv=1, causal=True),
+    "sq_ne_skv": lambda: synth.dense_case("x", "BNSD", 1, 2, 100, 128, "bf16", 37, skv=300),
+    "sq_ne_skv_causal": lambda: synth.dense_case("x", "BNSD", 1, 2, 300, 128, "bf16", 38, skv=100, causal=True),
+    "sink_causal": lambda: synth.dense_case("x", "BSND", 1, 3, 170, 128, "bf16", 39, sink=True, causal=True),
+    "band_pre5_next3_mask": lambda: _band_mask_case(40, 5, 3),
+    "band_pre0_next0_mask": lambda: _band_mask_case(41, 0, 0),
+    "band_neg_pre": lambda: _band_mask_case(42, -2, 9),
+    "causal_flag_band": lambda: synth.dense_case("x", "BNSD", 1, 2, 333, 128, "bf16", 43, causal=True,
+                                                 pre_tokens=70),
+    "random_mask_4d": lambda: _random_mask_case(44, (2, 1)),
+    "random_mask_bn": lambda: _random_mask_case(45, (1, 2)),
+    "fp32_varlen_sink": lambda: synth.varlen_case("x", [33, 0, 90], 2, 64, "fp32", 46, sink=True, causal=True),
+    "fp32_mask_band": lambda: _band_mask_case(47, 9, 0, dtype="fp32", d=64),
+    "fp32_d96": lambda: synth.dense_case("x", "BSND", 1, 2, 75, 96, "fp32", 48, dv=80),
+    "bf16_d96_generic": lambda: synth.dense_case("x", "BNSD", 1, 2, 99, 96, "bf16", 49),
+    "bf16_dv_lt_d_generic": lambda: synth.dense_case("x", "BNSD", 1, 2, 99, 128, "bf16", 50, dv=64),
+    "tnd_mask_2d": lambda: _tnd_mask_case(51),
+    "scale_zero": lambda: synth.dense_case("x", "BNSD", 1, 1, 130, 128, "bf16", 52, causal=True, scale=0.0),
+    "stats_same_as_input": lambda: synth.varlen_case("x", [64, 200], 2, 128, "bf16", 53, causal=True,
+                                                     softmax_out_layout="same_as_input"),
+    "len_1": lambda: synth.dense_case("x", "BNSD", 1, 2, 1, 128, "bf16", 54),
+    "len_63_65": lambda: synth.varlen_case("x", [63, 64, 65, 127, 128, 129], 2, 128, "bf16", 55),
+    "sink_neg_inf": lambda: _sink_neg_inf_case(56),
+    "large_logits": lambda: synth.dense_case("x", "BNSD", 1, 2, 200, 128, "bf16", 57, scale=1.0),
+}
+
+
+def _band_mask_case(seed, pre, nxt, dtype="bf16", d=128):
+    c = synth.dense_case("x", "BNSD", 1, 2, 230, d, dtype, seed)
+    i = torch.arange(230).view(-1, 1)
+    j = torch.arange(230).view(1, -1)
+    c.atten_mask = (((j - i) > nxt) | ((i - j) > pre)).to(torch.uint8)  # consistent with the window
+    c.pre_tokens, c.next_tokens = pre, nxt
+    return c
+
+
+def _random_mask_case(seed, bn):
+    c = synth.dense_case("x", "BNSD", 2, 2, 150, 128, "bf16", seed)
+    g = synth.generator(seed + 1000)
+    c.atten_mask = (torch.rand(bn[0], bn[1], 150, 150, generator=g) < 0.5).to(torch.bool)
+    c.atten_mask[..., 7, :] = True  # a row with no kept key
+    return c
+
+
+def _tnd_mask_case(seed):
+    c = synth.varlen_case("x", [100, 37, 140], 2, 128, "bf16", seed)
+    g = synth.generator(seed + 1000)
+    c.atten_mask = (torch.rand(160, 160, generator=g) < 0.3).to(torch.uint8)
+    return c
+
+
+def _sink_neg_inf_case(seed):
+    c = synth.dense_case("x", "BNSD", 1, 3, 90, 128, "bf16", seed, sink=True, causal=True)
+    c.sink = torch.tensor([float("-inf"), 0.5, float("-inf")])
+    return c
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_case(name):
+    case = SMALL[name]()
+    print(f"[parity] start {name} layout={case.layout} q={tuple(case.q.shape)} dtype={case.q.dtype}", flush=True)
+    _report(name, pu.compare_case(case))
+
+
+@pytest.mark.parametrize("layout", ["BSH", "SBH"])
+def test_hidden_layouts(layout):
+    base = synth.dense_case("x", "BNSD", 2, 3, 150, 128, "bf16", 60, causal=True)
+    case = synth.Case(name=layout, layout=layout, q=orc.from_bnsd(base.q, layout),
+                      k=orc.from_bnsd(base.k, layout), v=orc.from_bnsd(base.v, layout), scale=base.scale,
+                      causal=True)
+    _report(layout, pu.compare_case(case, heads=3))
+
+
+def test_noncontiguous_strides():
+    """Views with padded rows and heads go through the matrix-core path unchanged."""
+    g = synth.generator(61)
+    big = synth.normal((1, 200, 3, 136), g, "bf16")  # pad D 128 -> 136 (multiple of 8 elements)
+    q = big[..., :128]
+    k = synth.normal((1, 200, 3, 136), g, "bf16")[..., :128]
+    v = synth.normal((1, 200, 3, 136), g, "bf16")[..., :128]
+    case = synth.Case(name="strided", layout="BSND", q=q, k=k, v=v, scale=128**-0.5, causal=True)
+    qg, kg, vg = (big.cuda()[..., :128], k.contiguous().cuda(), v.contiguous().cuda())
+    plan = api.attention_forward(qg, kg, vg, scale=case.scale, causal=True, return_plan=True)
+    assert "kernel=mfma" in plan.describe(), plan.describe()
+    torch.cuda.synchronize()
+    O, _, _ = pu.run_oracle(case)
+    pu.check_output(plan.out.cpu(), O, torch.bfloat16)
+    plan.close()
+
+
+def test_misaligned_uses_generic_and_matches():
+    g = synth.generator(62)
+    flat = synth.normal((1 + 2 * 100 * 2 * 128,), g, "bf16")
+    q = flat[1:].view(2, 100, 2, 128)
+    case = synth.dense_case("x", "BSND", 2, 2, 100, 128, "bf16", 63)
+    case.q = q
+    qg = torch.empty(flat.numel(), dtype=torch.bfloat16, device="cuda")
+    qg.copy_(flat.cuda())
+    qg = qg[1:].view(2, 100, 2, 128)
+    plan = api.attention_forward(qg, case.k.cuda(), case.v.cuda(), scale=case.scale, return_plan=True)
+    assert "kernel=generic" in plan.describe()
+    torch.cuda.synchronize()
+    O, _, _ = pu.run_oracle(case)
+    pu.check_output(plan.out.cpu(), O, torch.bfloat16)
+    plan.close()
+
+
+# ---------------------------------------------------------------------------
+# determinism, guard bands, repeated plan execution
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c2_small_bf16", "c4_small_varlen", "c5_small_sink_rope"])
+def test_bitwise_deterministic(name):
+    case = SMALL[name]()
+    a = pu.run_gpu(case)
+    b = pu.run_gpu(case)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype != torch.float32 else x.view(torch.int32),
+                           y.view(torch.uint8) if y.dtype != torch.float32 else y.view(torch.int32))
+
+
+def test_guard_bands_untouched():
+    case = synth.workload("c4_varlen_causal", small=True)
+    T, N, D = case.q.shape
+    pad = 4096
+    poison = -12345.0
+    obuf = torch.full((pad + T * N * D + pad,), poison, dtype=torch.bfloat16, device="cuda")
+    out = obuf[pad:pad + T * N * D].view(T, N, D)
+    sbuf = torch.full((pad + N * T * 8 + pad,), poison, dtype=torch.float32, device="cuda")
+    smax = sbuf[pad:pad + N * T * 8].view(N, T, 8)
+    g = {k: pu.to_gpu(v) for k, v in case.tensors().items()}
+    plan = api.ForwardPlan(g["q"], g["k"], g["v"], layout="TND", scale=case.scale, head_num=N,
+                           cu_seqlens_q=g["cu_seqlens_q"], cu_seqlens_kv=g["cu_seqlens_kv"], causal=True, out=out,
+                           softmax_max=smax, softmax_sum=None)
+    plan.run()
+    torch.cuda.synchronize()
+    for buf in (obuf, sbuf):
+        assert bool((buf[:pad] == poison).all()) and bool((buf[-pad:] == poison).all())
+    assert not bool((out == poison).any())
+    O, M, _ = pu.run_oracle(case)
+    pu.check_output(out.cpu(), O, torch.bfloat16)
+    pu.check_stats(smax.cpu(), M, "max", torch.bfloat16)
+    plan.close()
+
+
+def test_plan_reuse_and_stream():
+    case = synth.workload("c2_dense_bsnd", "bf16", small=True)
+    g = {k: pu.to_gpu(v) for k, v in case.tensors().items()}
+    plan = api.attention_forward(g["q"], g["k"], g["v"], scale=case.scale, return_plan=True)
+    first = plan.out.clone()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        plan.out.zero_()
+        for _ in range(3):
+            plan.run()
+    s.synchronize()
+    assert torch.equal(first, plan.out)
+    plan.close()
+
+
+def test_v5_call_example_on_gpu():
+    """The V5 page's call-example inputs: all-ones bf16 q/k/v + rope, sink 3.0, scale 0.088388."""
+    T = 256
+    ones = lambda *s: torch.ones(*s, dtype=torch.bfloat16, device="cuda")
+    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    out, smax, ssum = api.attention_forward_varlen(
+        ones(T, 1, 128), ones(T, 1, 128), ones(T, 1, 128), cu, cu, softmax_scale=0.088388,
+        q_rope=ones(T, 1, 64), k_rope=ones(T, 1, 64), sink=torch.tensor([3.0], device="cuda"),
+        atten_mask=torch.zeros(T, T, dtype=torch.uint8, device="cuda"), pre_tokens=65536, next_tokens=65536,
+        softmax_out_layout="same_as_input", return_softmax_stats=True)
+    torch.cuda.synchronize()
+    s = 0.088388 * 192
+    m = max(s, 3.0)
+    l = T * math.exp(s - m) + math.exp(3.0 - m)
+    assert abs(float(smax[0, 0, 0]) - m) < 1e-3
+    assert abs(math.log(float(ssum[0, 0, 0])) - math.log(l)) < 1e-3
+    assert float((out.float() - 1.0).abs().max()) < 1e-2
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled rows
+# ---------------------------------------------------------------------------
+
+FULL = ["c2_bf16", "c2_fp16", "c3_causal", "c3_band", "c4_varlen_causal", "c5_varlen_sink_rope"]
+
+
+def _full_case(name):
+    if name == "c2_bf16":
+        return synth.workload("c2_dense_bsnd", "bf16")
+    if name == "c2_fp16":
+        return synth.workload("c2_dense_bsnd", "fp16")
+    return synth.workload(name)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    case = _full_case(name)
+    print(f"[parity] full {name} q={tuple(case.q.shape)}", flush=True)
+    o, smax, ssum = pu.run_gpu(case)
+    g = synth.generator(999)
+    if case.layout == "TND":
+        cu = case.cu_seqlens_q.tolist()
+        nseq, nh = len(cu) - 1, case.q.shape[1]
+        samples = []
+        for b in sorted({0, nseq - 1, nseq // 2}):
+            for h in sorted({0, nh - 1}):
+                samples.append((b, h, pu.sample_rows(cu[b + 1] - cu[b], 12, g)))
+    else:
+        B = case.q.shape[0]
+        nh = case.q.shape[1] if case.layout == "BNSD" else case.q.shape[2]
+        S = case.q.shape[2] if case.layout == "BNSD" else case.q.shape[1]
+        samples = [(b, h, pu.sample_rows(S, 12, g)) for b in sorted({0, B - 1}) for h in sorted({0, nh // 2, nh - 1})]
+    _report(name, pu.compare_sampled(case, samples, o, smax, ssum))
+    # properties at every row: finite, stats slots equal, l >= 1 where a key is kept
+    assert torch.isfinite(o.float()).all()
+    assert bool((smax == smax[..., :1]).all()) and bool((ssum == ssum[..., :1]).all())
+    assert bool((ssum[..., 0] >= 1.0 - 1e-6).all())
