@@ -61,6 +61,27 @@ struct MfmaCfg {
   static constexpr int NDT = DV / 32;                        // 32-wide output tiles
 };
 
+// Sum / max of a value with the same lane's partner in the other half-wave
+// (lane l <-> l ^ 32), one v_permlane32_swap: for (x, x) it returns the low
+// half's values in lanes 32..63 of the first result and the high half's in
+// lanes 0..31 of the second, so combining the two pairs every lane with its
+// partner.
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The reference max used in the exponentials only moves when a block's max
+// exceeds it by more than 2^kLazy (in log2 units), so most blocks skip the
+// rescale of the output accumulator.  Unnormalised weights stay <= 2^kLazy.
+// The true running max is tracked separately for softmaxMax, and the sum is
+// brought to it once at the end.
+constexpr float kLazy = 8.0f;
+
 template <typename T, int D, int DR>
 __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   using C = MfmaCfg<T, D, DR>;
@@ -79,17 +100,11 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   const bool row_ok = row < tl.sq;
   const int g = tl.h / p.group;
 
-  const T* __restrict__ qp = static_cast<const T*>(p.q);
-  const T* __restrict__ kp = static_cast<const T*>(p.k) + tl.b * p.k_sb + g * p.k_sh + tl.kv_row0 * p.k_ss;
-  const T* __restrict__ vp = static_cast<const T*>(p.v) + tl.b * p.v_sb + g * p.v_sh + tl.kv_row0 * p.v_ss;
-  const T* __restrict__ krp =
-      DR ? static_cast<const T*>(p.kr) + tl.b * p.kr_sb + g * p.kr_sh + tl.kv_row0 * p.kr_ss : nullptr;
-
   // ---- Q^T fragments (B operand): lane holds row `row`, dims 16*ks + 8*hh .. +7
   V8 qf[C::NKS];
   {
     const int64_t qrow = tl.q_row0 + (row_ok ? row : 0);
-    const T* qrowp = qp + tl.b * p.q_sb + tl.h * p.q_sh + qrow * p.q_ss;
+    const T* qrowp = static_cast<const T*>(p.q) + tl.b * p.q_sb + tl.h * p.q_sh + qrow * p.q_ss;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qrowp + 16 * ks + 8 * hh) : make_uint4(0, 0, 0, 0);
@@ -112,64 +127,80 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   const int jb0 = (kv_lo / BN) * BN;
   const int nblocks = (kv_hi >= kv_lo && last_row >= i0) ? (kv_hi - jb0) / BN + 1 : 0;
 
-  // ---- running state (log2 domain: m2 = max of scale*log2(e)*s)
+  // ---- running state, log2 domain: t = s * c, c = scale * log2(e)
   const float c = p.scale_log2;
-  float m2 = kNegInf, lsum = 0.f;
+  float m_ref = kNegInf;  // reference max of the exponentials
+  float m_max = kNegInf;  // true running max (for softmaxMax)
+  float lsum = 0.f;       // this half-wave's part of sum_j 2^(t_j - m_ref)
   if (p.has_sink) {
     const float sk = p.sink[tl.h];
     if (sk > kNegInf) {
-      m2 = sk * kLog2e;
-      lsum = hh == 0 ? 1.f : 0.f;  // e^(sink - m) = 1 at m = sink; counted once per row
+      m_ref = m_max = sk * kLog2e;
+      lsum = hh == 0 ? 1.f : 0.f;  // 2^(sink - m_ref) = 1, counted once per row
     }
   }
   f32x16 oacc[C::NDT];
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] = f32x16{};
 
-  // ---- global -> register staging of one key block
+  // ---- global -> register staging of one key block (per-thread addresses fixed up front)
+  const T* kbase = static_cast<const T*>(p.k) + tl.b * p.k_sb + g * p.k_sh + tl.kv_row0 * p.k_ss;
+  const T* vbase = static_cast<const T*>(p.v) + tl.b * p.v_sb + g * p.v_sh + tl.kv_row0 * p.v_ss;
+  const T* krbase =
+      DR ? static_cast<const T*>(p.kr) + tl.b * p.kr_sb + g * p.kr_sh + tl.kv_row0 * p.kr_ss : nullptr;
+  const T* kptr[C::KCHUNKS];
+  int64_t kstr[C::KCHUNKS];  // row stride of the tensor the chunk comes from (K or Krope)
+  int kkey[C::KCHUNKS];
+  int koff[C::KCHUNKS];      // LDS element offset within a stage
+#pragma unroll
+  for (int i = 0; i < C::KCHUNKS; ++i) {
+    const int ch = tid + i * kMfmaThreads;
+    const int key = ch / C::KCPR, col = ch - key * C::KCPR;
+    kkey[i] = key;
+    koff[i] = key * C::KS + col * 8;
+    if (DR == 0 || col < D / 8) {
+      kstr[i] = p.k_ss;
+      kptr[i] = kbase + (int64_t)key * p.k_ss + col * 8;
+    } else {
+      kstr[i] = p.kr_ss;
+      kptr[i] = krbase + (int64_t)key * p.kr_ss + (col - D / 8) * 8;
+    }
+  }
+  const int vkg = tid & 15, vdg = tid >> 4;  // V: keys 4*vkg..+3, dims 8*vdg..+7
+  const bool v_active = tid < C::VBLOCKS;
+  const T* vptr = vbase + (int64_t)(4 * vkg) * p.v_ss + 8 * vdg;
+  const int voff = C::K_ELEMS + (8 * vdg) * C::VS + vt_pos(4 * vkg);
+
   uint4 kreg[C::KCHUNKS];
   uint4 vreg[4];
-  const int vkg = tid & 15, vdg = tid >> 4;  // V: keys 4*vkg..+3, dims 8*vdg..+7
   auto load_block = [&](int jb) {
+    const bool full = jb + BN <= tl.skv;
 #pragma unroll
     for (int i = 0; i < C::KCHUNKS; ++i) {
-      const int ch = tid + i * kMfmaThreads;
-      const int key = ch / C::KCPR, col = ch - key * C::KCPR;
+      const T* a = kptr[i] + (int64_t)jb * kstr[i];
       uint4 u = make_uint4(0, 0, 0, 0);
-      if (key < BN && jb + key < tl.skv) {
-        const int64_t r = jb + key;
-        if (DR == 0 || col < D / 8)
-          u = *reinterpret_cast<const uint4*>(kp + r * p.k_ss + col * 8);
-        else
-          u = *reinterpret_cast<const uint4*>(krp + r * p.kr_ss + (col - D / 8) * 8);
-      }
+      if (kkey[i] < BN && (full || jb + kkey[i] < tl.skv)) u = *reinterpret_cast<const uint4*>(a);
       kreg[i] = u;
     }
-    if (tid < C::VBLOCKS) {
+    if (v_active) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = jb + 4 * vkg + r;
-        vreg[r] = key < tl.skv ? *reinterpret_cast<const uint4*>(vp + (int64_t)key * p.v_ss + 8 * vdg)
-                               : make_uint4(0, 0, 0, 0);
+        const T* a = vptr + (int64_t)(jb + r) * p.v_ss;
+        vreg[r] = (full || jb + 4 * vkg + r < tl.skv) ? *reinterpret_cast<const uint4*>(a) : make_uint4(0, 0, 0, 0);
       }
     }
   };
   auto store_block = [&](int stage) {
-    T* ks_ = smem + stage * C::STAGE;
-    T* vs_ = ks_ + C::K_ELEMS;
+    T* st = smem + stage * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < C::KCHUNKS; ++i) {
-      const int ch = tid + i * kMfmaThreads;
-      const int key = ch / C::KCPR, col = ch - key * C::KCPR;
-      if (key < BN) *reinterpret_cast<uint4*>(ks_ + key * C::KS + col * 8) = kreg[i];
-    }
-    if (tid < C::VBLOCKS) {
+    for (int i = 0; i < C::KCHUNKS; ++i)
+      if (kkey[i] < BN) *reinterpret_cast<uint4*>(st + koff[i]) = kreg[i];
+    if (v_active) {
       // 4 keys x 8 dims -> 8 dims x 4 keys (pairs of 16-bit lanes regrouped)
       const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
       const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
       const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
       const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-      const int pos = vt_pos(4 * vkg);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1;
@@ -181,12 +212,12 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
           lo = (w0[w] & 0xffffu) | (w1[w] << 16);
           hi = (w2[w] & 0xffffu) | (w3[w] << 16);
         }
-        *reinterpret_cast<uint2*>(vs_ + (8 * vdg + e) * C::VS + pos) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>(st + voff + e * C::VS) = make_uint2(lo, hi);
       }
     }
   };
 
-  // mask element address base (b, h) for this lane's row
+  // mask row of this lane (dense: [b|0, h|0, row, :]; TND: the 2-D mask in local coordinates)
   const uint8_t* mrow = nullptr;
   if (p.has_mask) {
     if (p.varlen)
@@ -221,14 +252,12 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
       }
     }
 
-    // ---- which keys survive (only blocks crossing an edge pay per-element tests)
+    // ---- blocks crossing the window edge, the sequence end, or needing the mask:
+    // excluded scores become -inf (weight exactly 0 below)
     const bool tail = jb + BN > tl.skv;
     const bool edge = p.band && !(jb >= last_row - p.pre && jb + BN - 1 <= i0 + p.next);
     const bool read_mask = p.has_mask && (p.mask_everywhere || edge || tail);
-    const bool partial = tail || edge || read_mask;
-    uint32_t keep = 0xffffffffu;  // bit 16*t + j: element j of tile t
-    if (partial) {
-      keep = 0;
+    if (tail || edge || read_mask) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -242,7 +271,7 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
             else
               k_ok = mrow[(int64_t)key * p.m_sk] == 0;
           }
-          keep |= (k_ok ? 1u : 0u) << (16 * t + j);
+          sacc[t][j] = k_ok ? sacc[t][j] : kNegInf;
         }
       }
     }
@@ -252,30 +281,28 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float s = sacc[t][j];
-        mx = fmaxf(mx, ((keep >> (16 * t + j)) & 1u) ? s : kNegInf);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m2, mx * c);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m2 - m_use);
-    m2 = m_new;
+      for (int j = 0; j < 16; ++j) mx = __builtin_fmaxf(mx, sacc[t][j]);
+    mx = xhalf_max(mx);
+    const float mxc = mx * c;  // c > 0, so -inf stays -inf
+    m_max = __builtin_fmaxf(m_max, mxc);
+    if (mxc > m_ref + kLazy) {
+      const float alpha = fast_exp2(m_ref - mxc);  // 0 when m_ref = -inf
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] *= alpha;
+      m_ref = mxc;
+    }
+    const float m_use = m_ref == kNegInf ? 0.f : m_ref;
 
     V8 pk[2][2];
-    float ps = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        float e = fast_exp2(fmaf(sacc[t][j], c, -m_use));
-        e = ((keep >> (16 * t + j)) & 1u) ? e : 0.f;
-        ps += e;
+        const float e = fast_exp2(fmaf(sacc[t][j], c, -m_use));
+        lsum += e;
         pk[t][j >> 3][j & 7] = from_f32<T>(e);
       }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] *= alpha;
 
     // ---- O^T += V^T P^T
 #pragma unroll
@@ -294,10 +321,10 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
     __syncthreads();
   }
 
-  // ---- epilogue: O = O / l, statistics
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  // ---- epilogue: O = O / l, statistics at the true max
+  const float lref = xhalf_sum(lsum);
   if (!row_ok) return;
-  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  const float inv = lref > 0.f ? 1.f / lref : 0.f;
   const int64_t orow = tl.q_row0 + row;
   T* op = static_cast<T*>(p.o) + tl.b * p.o_sb + tl.h * p.o_sh + orow * p.o_ss;
 #pragma unroll
@@ -313,9 +340,10 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   }
   if (p.smax || p.ssum) {
     const int64_t so = tl.b * p.st_sb + tl.h * p.st_sh + orow * p.st_ss + 4 * hh;
-    const float mnat = m2 == kNegInf ? kNegInf : m2 * kLn2;
+    const float mnat = m_max == kNegInf ? kNegInf : m_max * kLn2;
+    const float ltrue = lref > 0.f ? lref * fast_exp2(m_ref - m_max) : 0.f;
     if (p.smax) *reinterpret_cast<float4*>(p.smax + so) = make_float4(mnat, mnat, mnat, mnat);
-    if (p.ssum) *reinterpret_cast<float4*>(p.ssum + so) = make_float4(ltot, ltot, ltot, ltot);
+    if (p.ssum) *reinterpret_cast<float4*>(p.ssum + so) = make_float4(ltrue, ltrue, ltrue, ltrue);
   }
 }
 

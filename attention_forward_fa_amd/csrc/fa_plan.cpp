@@ -366,7 +366,11 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   p.dr = (int32_t)dr;
   p.dv = (int32_t)v.d;
   p.scale = (float)scale_value;
+  // The kernels turn excluded scores into -inf and rely on -inf * c = -inf;
+  // a zero scale is replaced by a positive one far below any score's
+  // resolution (every weight is then exactly 1, as with scale 0).
   p.scale_log2 = (float)(scale_value * 1.4426950408889634);
+  if (!(p.scale_log2 > 1e-30f)) p.scale_log2 = 1e-30f;
   p.band = band;
   p.pre = (int32_t)pre;
   p.next = (int32_t)nxt;

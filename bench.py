@@ -1,0 +1,339 @@
+"""Benchmark: FlashAttention forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype bf16|fp16]
+
+A step is one pass of the forward over one batch of synthetic input: phase 1
+(plan) and phase 2 (the HIP kernels) of ``libfa_fwd.so``.  Inputs are resident
+in GPU memory before the timed region.  The default workload is dense BSND
+B=2 S=4096 N=24 D=128 in bf16 with no mask, scale 1/sqrt(128).
+
+Prints one JSON line.  ``value`` is TFLOP/s over the timed steps, counting
+4*D FLOP per kept (query, key) pair (2*(D+Dr) + 2*Dv with rope parts), with
+kept pairs counted on 128x128 blocks as the workloads' accounting asks.
+``roofline`` prices the forward kernel's average duration, measured with HIP
+events on the launch stream during the timed region, against the MI355X dense
+matrix peak.  ``cpu_baseline`` times the CPU float64 oracle on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s + % of MI355X bf16 MFMA peak, B2 S4096 N24 D128"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+HBM_GBPS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+KERNEL_SOURCES = ["fa_mfma.hpp", "fa_device.hpp", "fa_params.h", "fa_mfma_bf16.hip", "fa_mfma_f16.hip",
+                  "fa_generic.hip", "fa_launch.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "attention_forward_fa_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2_dense_bsnd",
+                    choices=["c2_dense_bsnd", "c3_causal", "c3_band", "c4_varlen_causal", "c5_varlen_sink_rope"])
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true", help="also time the kernel after evicting caches")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="launch one device copy of this many MiB (counter calibration runs)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# FLOP and byte accounting
+# ---------------------------------------------------------------------------
+
+def kept_pairs(case, block: int = 0) -> int:
+    """Kept (query, key) pairs; with block > 0, count whole block x block tiles that keep any pair."""
+    import torch
+
+    def seq_pairs(sq, skv):
+        if sq == 0 or skv == 0:
+            return 0
+        band = case.atten_mask is not None or case.causal
+        pre = case.pre_tokens if band else None
+        nxt = (min(case.next_tokens, 0) if case.causal else case.next_tokens) if band else None
+        if block == 0:
+            i = torch.arange(sq, dtype=torch.int64)
+            lo = torch.zeros_like(i) if pre is None else (i - pre).clamp(min=0)
+            hi = torch.full_like(i, skv - 1) if nxt is None else (i + nxt).clamp(max=skv - 1)
+            return int((hi - lo + 1).clamp(min=0).sum())
+        total = 0
+        for ib in range(0, sq, block):
+            i0, i1 = ib, min(ib + block, sq) - 1
+            lo = 0 if pre is None else max(0, i0 - pre)
+            hi = skv - 1 if nxt is None else min(skv - 1, i1 + nxt)
+            if hi < lo:
+                continue
+            jb0 = (lo // block) * block
+            for jb in range(jb0, hi + 1, block):
+                total += (i1 - i0 + 1) * (min(jb + block, skv) - jb)
+        return total
+
+    if case.layout == "TND":
+        cu_q = case.cu_seqlens_q.tolist()
+        cu_k = case.cu_seqlens_kv.tolist()
+        per_head = sum(seq_pairs(cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]) for b in range(len(cu_q) - 1))
+        heads = case.q.shape[1]
+        return per_head * heads
+    B = case.q.shape[0]
+    heads = case.q.shape[1] if case.layout == "BNSD" else case.q.shape[2]
+    sq = case.q.shape[2] if case.layout == "BNSD" else case.q.shape[1]
+    skv = case.k.shape[2] if case.layout == "BNSD" else case.k.shape[1]
+    return seq_pairs(sq, skv) * B * heads
+
+
+def flops_per_pair(case) -> int:
+    d = case.q.shape[-1]
+    dr = case.q_rope.shape[-1] if case.q_rope is not None else 0
+    dv = case.v.shape[-1]
+    return 2 * (d + dr) + 2 * dv
+
+
+def algorithmic_bytes(case) -> int:
+    """Inputs read once, output and statistics written once."""
+    tot = 0
+    for t in (case.q, case.k, case.v, case.q_rope, case.k_rope, case.atten_mask, case.sink):
+        if t is not None:
+            tot += t.numel() * t.element_size()
+    tot += case.q.numel() // case.q.shape[-1] * case.v.shape[-1] * case.q.element_size()  # O
+    rows = case.q.numel() // case.q.shape[-1]
+    tot += 2 * rows * 8 * 4  # softmax max / sum, 8 fp32 slots each
+    return tot
+
+
+def load_traffic(src_hash: str, workload: str, dtype: str):
+    """HBM bytes per launch from committed rocprofv3 counters, if taken on this kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        data = json.load(f)
+    rec = data.get(f"{workload}:{dtype}")
+    if not rec or rec.get("kernel_source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(case, budget_s: float):
+    import torch
+
+    from oracle import attention as orc
+
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    B = case.q.shape[0] if case.layout != "TND" else 1
+    heads = case.q.shape[2] if case.layout == "BSND" else case.q.shape[1]
+    done_pairs, units, t0 = 0, 0, time.perf_counter()
+    fpp = flops_per_pair(case)
+    if case.layout == "TND":
+        cu = case.cu_seqlens_q.tolist()
+        work = [(b, h) for b in range(len(cu) - 1) for h in range(heads)]
+    else:
+        work = [(b, h) for b in range(B) for h in range(heads)]
+    for (b, h) in work:
+        if case.layout == "TND":
+            n = int(cu[b + 1] - cu[b])
+        else:
+            n = case.q.shape[1] if case.layout == "BSND" else case.q.shape[2]
+        rows = torch.arange(n)
+        orc.attention_forward(case.q, case.k, case.v, layout=case.layout, scale=case.scale, q_rope=case.q_rope,
+                              k_rope=case.k_rope, atten_mask=case.atten_mask, sink=case.sink, causal=case.causal,
+                              pre_tokens=case.pre_tokens, next_tokens=case.next_tokens,
+                              cu_seqlens_q=case.cu_seqlens_q, cu_seqlens_kv=case.cu_seqlens_kv,
+                              samples=[(b, h, rows)])
+        units += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    total_pairs = kept_pairs(case, block=128)
+    pairs = total_pairs * units / len(work)
+    tflops = pairs * fpp / dt / 1e12
+    cpu = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{units} of {len(work)} (sequence, head) pairs, every query row, float64, {dt:.1f} s; "
+                      f"FLOPs scaled by the same 128x128 block accounting; CPU: {cpu}"}
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(head / batch sharding needs no collective; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from attention_forward_fa_amd import _lib, api
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    case = synth.workload(args.workload, args.dtype) if args.workload == "c2_dense_bsnd" else \
+        synth.workload(args.workload)
+    dtype = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[case.q.dtype]
+    g = {k: (v.to(dev) if v is not None else None) for k, v in case.tensors().items()}
+    nheads = case.q.shape[1] if case.layout in ("BNSD", "TND") else case.q.shape[2]
+    out = torch.empty(case.q.shape[:-1] + (case.v.shape[-1],), dtype=case.q.dtype, device=dev)
+    if case.layout == "TND":
+        T = case.q.shape[0]
+        smax = torch.empty(nheads, T, 8, dtype=torch.float32, device=dev)
+    else:
+        B = case.q.shape[0]
+        S = case.q.shape[2] if case.layout == "BNSD" else case.q.shape[1]
+        smax = torch.empty(B, nheads, S, 8, dtype=torch.float32, device=dev)
+    ssum = torch.empty_like(smax)
+
+    def make_plan():
+        return api.ForwardPlan(g["q"], g["k"], g["v"], layout=case.layout, scale=case.scale, head_num=nheads,
+                               query_rope=g["q_rope"], key_rope=g["k_rope"], atten_mask=g["atten_mask"],
+                               sink=g["sink"], cu_seqlens_q=g["cu_seqlens_q"], cu_seqlens_kv=g["cu_seqlens_kv"],
+                               causal=case.causal, pre_tokens=case.pre_tokens, next_tokens=case.next_tokens,
+                               softmax_out_layout=case.softmax_out_layout, out=out, softmax_max=smax,
+                               softmax_sum=ssum)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {args.copy_calibration_mib} MiB read + written", file=sys.stderr)
+        del a, b
+
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    plan0 = make_plan()
+    desc = plan0.describe()
+    ws = plan0.workspace
+    plan0.close()
+
+    def step(ev_pair=None):
+        # phase 1 + phase 2; the workspace is allocated once, outside the timed region
+        wsz, h = _lib.fa_fwd_get_workspace_size(
+            g["q"], g["q_rope"], g["k"], g["k_rope"], g["v"], None, g["atten_mask"], g["sink"], g["cu_seqlens_q"],
+            g["cu_seqlens_kv"], case.scale, 1.0, case.pre_tokens, case.next_tokens, nheads, case.layout, 0, 0,
+            case.causal, case.softmax_out_layout, smax, ssum, out)
+        if ev_pair is not None:
+            ev_pair[0].record(stream)
+        _lib.fa_fwd(ws, wsz, h, sh)
+        if ev_pair is not None:
+            ev_pair[1].record(stream)
+        _lib.fa_plan_destroy(h)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in events]
+    kernel_ms_avg = sum(kernel_ms) / len(kernel_ms)
+    kernel_ms_med = sorted(kernel_ms)[len(kernel_ms) // 2]
+
+    pairs_blk = kept_pairs(case, block=128)
+    pairs_exact = kept_pairs(case, block=0)
+    fpp = flops_per_pair(case)
+    flops = pairs_blk * fpp
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+    achieved = flops / (kernel_ms_avg * 1e-3) / 1e12
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(src_hash, args.workload, dtype)
+    abytes = algorithmic_bytes(case)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic: iid N(0,1) q/k/v drawn in fp32 from a fixed seed, rounded to the dtype",
+        "config": {"workload": args.workload, "layout": case.layout, "q_shape": list(case.q.shape),
+                   "causal": case.causal, "mask": case.atten_mask is not None,
+                   "pre_tokens": case.pre_tokens, "next_tokens": case.next_tokens,
+                   "rope_dim": case.q_rope.shape[-1] if case.q_rope is not None else 0,
+                   "sink": case.sink is not None, "scale": case.scale},
+        "pct_of_mfma_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic},
+        "kernel": {"name": "fa_fwd_mfma" if "kernel=mfma" in desc else "fa_fwd_generic", "plan": desc,
+                   "avg_ms": round(kernel_ms_avg, 5), "median_ms": round(kernel_ms_med, 5),
+                   "flops_per_launch": flops, "flops_exact_pairs": pairs_exact * fpp,
+                   "algorithmic_bytes_per_launch": abytes,
+                   "achieved_GBps_algorithmic": round(abytes / (kernel_ms_avg * 1e-3) / 1e9, 1),
+                   "source_hash": src_hash},
+    }
+    if args.cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(max(5, args.steps // 5)):
+            flush.fill_(1)
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            step(ev)
+            torch.cuda.synchronize()
+            cold.append(ev[0].elapsed_time(ev[1]))
+        cold_ms = sorted(cold)[len(cold) // 2]
+        result["kernel"]["cold_median_ms"] = round(cold_ms, 5)
+        result["kernel"]["cold_tflops"] = round(flops / (cold_ms * 1e-3) / 1e12, 2)
+    print(f"[bench] {args.workload} {dtype}: {value:.1f} TFLOP/s, kernel {kernel_ms_avg:.4f} ms avg", file=sys.stderr,
+          flush=True)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
