@@ -54,8 +54,8 @@ struct MfmaCfg {
   static constexpr int K_ELEMS = BN * KS;
   static constexpr int V_ELEMS = DV * VS;
   static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int KCPR = DK / 8;                        // 16-byte chunks per K row
-  static constexpr int KCHUNKS = (BN * KCPR + kMfmaThreads - 1) / kMfmaThreads;  // per thread
+  static constexpr int KCH = BN * D / 8 / kMfmaThreads;     // 16-byte K chunks per thread
+  static constexpr int KRCH = BN * DR / 8 / kMfmaThreads;    // 16-byte Krope chunks per thread
   static constexpr int VBLOCKS = (BN / 4) * (DV / 8);        // 4-key x 8-dim blocks per step
   static constexpr int NKS = DK / 16;                        // MFMA k-steps of the score product
   static constexpr int NDT = DV / 32;                        // 32-wide output tiles
@@ -143,58 +143,71 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] = f32x16{};
 
-  // ---- global -> register staging of one key block (per-thread addresses fixed up front)
+  // ---- global -> register staging of one key block.  Buffer loads: each
+  // block gets a scalar descriptor based at its first row whose size covers
+  // only the rows left in the sequence, so rows past the end read as zero with
+  // no branch; the per-lane byte offsets are fixed for the whole loop.
   const T* kbase = static_cast<const T*>(p.k) + tl.b * p.k_sb + g * p.k_sh + tl.kv_row0 * p.k_ss;
   const T* vbase = static_cast<const T*>(p.v) + tl.b * p.v_sb + g * p.v_sh + tl.kv_row0 * p.v_ss;
   const T* krbase =
       DR ? static_cast<const T*>(p.kr) + tl.b * p.kr_sb + g * p.kr_sh + tl.kv_row0 * p.kr_ss : nullptr;
-  const T* kptr[C::KCHUNKS];
-  int64_t kstr[C::KCHUNKS];  // row stride of the tensor the chunk comes from (K or Krope)
-  int kkey[C::KCHUNKS];
-  int koff[C::KCHUNKS];      // LDS element offset within a stage
+  const int64_t krow_b = p.k_ss * (int64_t)sizeof(T), vrow_b = p.v_ss * (int64_t)sizeof(T);
+  const int64_t krrow_b = DR ? p.kr_ss * (int64_t)sizeof(T) : 0;
+  uint32_t kvoff[C::KCH], kloff[C::KCH];    // K: global byte offset in the block, LDS element offset
+  uint32_t krvoff[C::KRCH + 1], krloff[C::KRCH + 1];
 #pragma unroll
-  for (int i = 0; i < C::KCHUNKS; ++i) {
+  for (int i = 0; i < C::KCH; ++i) {
     const int ch = tid + i * kMfmaThreads;
-    const int key = ch / C::KCPR, col = ch - key * C::KCPR;
-    kkey[i] = key;
-    koff[i] = key * C::KS + col * 8;
-    if (DR == 0 || col < D / 8) {
-      kstr[i] = p.k_ss;
-      kptr[i] = kbase + (int64_t)key * p.k_ss + col * 8;
-    } else {
-      kstr[i] = p.kr_ss;
-      kptr[i] = krbase + (int64_t)key * p.kr_ss + (col - D / 8) * 8;
-    }
+    const int key = ch / (D / 8), col = ch % (D / 8);
+    kvoff[i] = (uint32_t)(key * krow_b + col * 16);
+    kloff[i] = key * C::KS + col * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < C::KRCH; ++i) {
+    const int ch = tid + i * kMfmaThreads;
+    const int key = ch / (DR / 8), col = ch % (DR / 8);
+    krvoff[i] = (uint32_t)(key * krrow_b + col * 16);
+    krloff[i] = key * C::KS + D + col * 8;
   }
   const int vkg = tid & 15, vdg = tid >> 4;  // V: keys 4*vkg..+3, dims 8*vdg..+7
   const bool v_active = tid < C::VBLOCKS;
-  const T* vptr = vbase + (int64_t)(4 * vkg) * p.v_ss + 8 * vdg;
+  uint32_t vvoff[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) vvoff[r] = (uint32_t)((4 * vkg + r) * vrow_b + 16 * vdg);
   const int voff = C::K_ELEMS + (8 * vdg) * C::VS + vt_pos(4 * vkg);
 
-  uint4 kreg[C::KCHUNKS];
+  auto rsrc = [](const void* base, int64_t bytes) {
+    const int n = (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+  };
+  uint4 kreg[C::KCH];
+  uint4 krreg[C::KRCH + 1];
   uint4 vreg[4];
   auto load_block = [&](int jb) {
-    const bool full = jb + BN <= tl.skv;
+    const int64_t rows = min(tl.skv - jb, BN);  // >= 1 for every visited block
+    const auto rk = rsrc(kbase + (int64_t)jb * p.k_ss, rows * krow_b);
 #pragma unroll
-    for (int i = 0; i < C::KCHUNKS; ++i) {
-      const T* a = kptr[i] + (int64_t)jb * kstr[i];
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (kkey[i] < BN && (full || jb + kkey[i] < tl.skv)) u = *reinterpret_cast<const uint4*>(a);
-      kreg[i] = u;
+    for (int i = 0; i < C::KCH; ++i)
+      kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, kvoff[i], 0, 0));
+    if constexpr (DR > 0) {
+      const auto rkr = rsrc(krbase + (int64_t)jb * p.kr_ss, rows * krrow_b);
+#pragma unroll
+      for (int i = 0; i < C::KRCH; ++i)
+        krreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rkr, krvoff[i], 0, 0));
     }
     if (v_active) {
+      const auto rv = rsrc(vbase + (int64_t)jb * p.v_ss, rows * vrow_b);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const T* a = vptr + (int64_t)(jb + r) * p.v_ss;
-        vreg[r] = (full || jb + 4 * vkg + r < tl.skv) ? *reinterpret_cast<const uint4*>(a) : make_uint4(0, 0, 0, 0);
-      }
+      for (int r = 0; r < 4; ++r)
+        vreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vvoff[r], 0, 0));
     }
   };
   auto store_block = [&](int stage) {
     T* st = smem + stage * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < C::KCHUNKS; ++i)
-      if (kkey[i] < BN) *reinterpret_cast<uint4*>(st + koff[i]) = kreg[i];
+    for (int i = 0; i < C::KCH; ++i) *reinterpret_cast<uint4*>(st + kloff[i]) = kreg[i];
+#pragma unroll
+    for (int i = 0; i < C::KRCH; ++i) *reinterpret_cast<uint4*>(st + krloff[i]) = krreg[i];
     if (v_active) {
       // 4 keys x 8 dims -> 8 dims x 4 keys (pairs of 16-bit lanes regrouped)
       const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
@@ -230,12 +243,48 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
     load_block(jb0);
     store_block(0);
   }
+  // Wait here once for the Q fragments (and the first block): otherwise the
+  // compiler cannot prove they landed and re-waits for every outstanding load,
+  // including the next block's prefetch, at the top of each iteration.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   __syncthreads();
 
   for (int it = 0; it < nblocks; ++it) {
     const int jb = jb0 + it * BN;
     const int stg = it & 1;
     const bool more = it + 1 < nblocks;
+
+    // ---- blocks crossing the window edge or the sequence end, or needing the
+    // mask, test each element.  Mask bytes are fetched first so that waiting
+    // for them does not also wait for the next block's prefetch.
+    const bool tail = jb + BN > tl.skv;
+    const bool edge = p.band && !(jb >= last_row - p.pre && jb + BN - 1 <= i0 + p.next);
+    const bool read_mask = p.has_mask && (p.mask_everywhere || edge || tail);
+    uint32_t mw[8];  // mask bytes of keys jb + 32t + 8a + 4hh + 0..3, word 4t + a
+    if (read_mask) {
+      if (p.mask_vec4) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int key = jb + 32 * (w >> 2) + 8 * (w & 3) + 4 * hh;
+          mw[w] = (row_ok && key < tl.skv) ? *reinterpret_cast<const uint32_t*>(mrow + key) : 0u;
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int key = jb + 32 * (w >> 2) + 8 * (w & 3) + 4 * hh + b;
+            uint32_t byte = 0;
+            if (mrow != nullptr && key < tl.skv && (!p.varlen || key < p.m_cols)) byte = mrow[(int64_t)key * p.m_sk];
+            else if (p.varlen) byte = 1;  // outside the 2-D mask: excluded
+            v |= (byte ? 0xffu : 0u) << (8 * b);
+          }
+          mw[w] = v;
+        }
+      }
+    }
+
     if (more) load_block(jb + BN);
 
     const T* ks_ = smem + stg * C::STAGE;
@@ -252,11 +301,7 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
       }
     }
 
-    // ---- blocks crossing the window edge, the sequence end, or needing the mask:
     // excluded scores become -inf (weight exactly 0 below)
-    const bool tail = jb + BN > tl.skv;
-    const bool edge = p.band && !(jb >= last_row - p.pre && jb + BN - 1 <= i0 + p.next);
-    const bool read_mask = p.has_mask && (p.mask_everywhere || edge || tail);
     if (tail || edge || read_mask) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -265,12 +310,7 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
           const int key = jb + 32 * t + 8 * (j >> 2) + 4 * hh + (j & 3);
           bool k_ok = key < tl.skv;
           if (p.band) k_ok = k_ok && (key - row <= p.next) && (row - key <= p.pre);
-          if (read_mask && k_ok) {
-            if (p.varlen)
-              k_ok = mrow != nullptr && key < p.m_cols && mrow[(int64_t)key * p.m_sk] == 0;
-            else
-              k_ok = mrow[(int64_t)key * p.m_sk] == 0;
-          }
+          if (read_mask) k_ok = k_ok && ((mw[4 * t + (j >> 2)] >> (8 * (j & 3))) & 0xffu) == 0;
           sacc[t][j] = k_ok ? sacc[t][j] : kNegInf;
         }
       }

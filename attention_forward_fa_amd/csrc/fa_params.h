@@ -60,6 +60,7 @@ struct Params {
   int32_t band;      // window active (mask given or causal)
   int32_t has_mask, has_sink, varlen;
   int32_t mask_everywhere;  // read the mask in every block (window cuts nothing)
+  int32_t mask_vec4;        // dense mask with contiguous, 4-byte aligned rows: read 4 keys at once
 
   int32_t tiles_per_head;   // dense: ceil(sq / BM); TND: ceil(tq / BM) + nbatch (upper bound)
   int32_t num_wg;           // grid size

@@ -381,6 +381,8 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   const int64_t max_rows = q.s, max_keys = k.s;  // per-sequence lengths are at most these
   const bool window_cuts = band && (pre < max_rows - 1 || nxt < max_keys - 1);
   p.mask_everywhere = p.has_mask && !window_cuts;
+  p.mask_vec4 = p.has_mask && !p.varlen && p.m_sk == 1 && (reinterpret_cast<uintptr_t>(p.mask) & 3u) == 0 &&
+                p.m_sq % 4 == 0 && p.m_sb % 4 == 0 && p.m_sh % 4 == 0;
   p.reverse_tiles = band && nxt < max_keys - 1;
 
   const int64_t bm = pl->bm;
