@@ -44,8 +44,11 @@ def _run(cmd):
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source and link the library.  Always rebuilds."""
+    """Compile every source and link the library.  Always rebuilds; a failed
+    build leaves no library behind (never a stale one)."""
     os.makedirs(BUILD, exist_ok=True)
+    if os.path.exists(LIB):
+        os.remove(LIB)
     cmds = []
     objs = []
     for src in HIP_SOURCES:

@@ -10,6 +10,8 @@ namespace fa {
 
 hipError_t launch_mfma_bf16(const Params& p, hipStream_t s);
 hipError_t launch_mfma_f16(const Params& p, hipStream_t s);
+hipError_t launch_mfma_pp_bf16(const Params& p, hipStream_t s);
+hipError_t launch_mfma_pp_f16(const Params& p, hipStream_t s);
 hipError_t launch_generic(const Params& p, int dtype, hipStream_t s);
 
 }  // namespace fa

@@ -71,7 +71,9 @@ extern "C" fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_p
     if (e != hipSuccess) return runtime_fail("tile prefix launch", e);
   }
   hipError_t e;
-  if (plan->kind == fa::KERNEL_MFMA)
+  if (plan->kind == fa::KERNEL_MFMA_PP)
+    e = plan->dtype == FA_DTYPE_BF16 ? fa::launch_mfma_pp_bf16(p, s) : fa::launch_mfma_pp_f16(p, s);
+  else if (plan->kind == fa::KERNEL_MFMA)
     e = plan->dtype == FA_DTYPE_BF16 ? fa::launch_mfma_bf16(p, s) : fa::launch_mfma_f16(p, s);
   else
     e = fa::launch_generic(p, plan->dtype, s);

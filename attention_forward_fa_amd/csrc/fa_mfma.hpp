@@ -21,8 +21,14 @@
 // per-lane scalar.  The accumulator layout of S^T is reused as the B operand
 // of the second product without any data movement: the 16 keys of one MFMA
 // k-step are {0-3, 8-11} in the low half-wave and {4-7, 12-15} in the high
-// one.  V is stored transposed in LDS with bits 2 and 3 of the key index
-// swapped, so that the same key order is one contiguous 16-byte read.
+// one.
+//
+// K and V blocks go from global memory straight into LDS (buffer loads with
+// an LDS destination: no staging registers, no LDS stores), row-major as in
+// memory, with the 16-byte units of each row XOR-swizzled by the row index so
+// the operand reads hit distinct banks.  The V^T operand is read with the
+// transposing LDS load (ds_read_tr16_b64), which hands each lane 4 keys of
+// one column, so V is never transposed explicitly.
 #pragma once
 
 #include "fa_device.hpp"
@@ -40,26 +46,39 @@ __device__ __forceinline__ f32x16 mfma32<_Float16>(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// Position of key k inside a 64-key block of the transposed V tile.
-__device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
-
 template <typename T, int D, int DR>
 struct MfmaCfg {
-  static constexpr int BM = kMfmaBM;      // query rows per workgroup
-  static constexpr int BN = kMfmaBN;      // keys per step
-  static constexpr int DK = D + DR;       // score reduction length
+  static constexpr int BM = kMfmaBM;       // query rows per workgroup
+  static constexpr int BN = kMfmaBN;       // keys per step
+  static constexpr int DK = D + DR;        // score reduction length
   static constexpr int DV = D;
-  static constexpr int KS = DK + 8;       // K row stride in LDS (elements); +16 B breaks bank aliasing
-  static constexpr int VS = BN + 8;       // V^T row stride in LDS (elements)
-  static constexpr int K_ELEMS = BN * KS;
-  static constexpr int V_ELEMS = DV * VS;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int KCH = BN * D / 8 / kMfmaThreads;     // 16-byte K chunks per thread
-  static constexpr int KRCH = BN * DR / 8 / kMfmaThreads;    // 16-byte Krope chunks per thread
-  static constexpr int VBLOCKS = (BN / 4) * (DV / 8);        // 4-key x 8-dim blocks per step
+  static constexpr int KU = D / 8;         // 16-byte units per K row
+  static constexpr int KRU = DR / 8;       // units per Krope row
+  static constexpr int VU = DV / 8;        // units per V row
+  static constexpr int K_BYTES = BN * KU * 16;
+  static constexpr int KR_BYTES = BN * KRU * 16;
+  static constexpr int V_BYTES = BN * VU * 16;
+  static constexpr int KR_OFF = K_BYTES;             // byte offsets within a stage
+  static constexpr int V_OFF = K_BYTES + KR_BYTES;
+  static constexpr int STAGE_BYTES = K_BYTES + KR_BYTES + V_BYTES;
+  static constexpr int K_LOADS = BN * KU / kMfmaThreads;    // 16-byte loads per thread per block
+  static constexpr int KR_LOADS = BN * KRU / kMfmaThreads;
+  static constexpr int V_LOADS = BN * VU / kMfmaThreads;
   static constexpr int NKS = DK / 16;                        // MFMA k-steps of the score product
   static constexpr int NDT = DV / 32;                        // 32-wide output tiles
 };
+
+// Physical 16-byte unit of logical unit u in LDS row r.  K rows: reads of 8
+// consecutive rows at one unit (one ds_read_b128 quarter-wave) land on 8
+// different units.  V rows: the transposing reads touch 4 consecutive rows at
+// an even/odd unit pair; an even XOR keeps the pair contiguous and spreads the
+// 4 rows over distinct banks.
+__device__ __forceinline__ int k_swz(int r, int u) { return u ^ (r & 7); }
+template <int VU>
+__device__ __forceinline__ int v_swz(int r, int u) { return VU >= 16 ? u ^ ((r & 7) << 1) : u ^ ((r & 3) << 1); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Sum / max of a value with the same lane's partner in the other half-wave
 // (lane l <-> l ^ 32), one v_permlane32_swap: for (x, x) it returns the low
@@ -82,12 +101,218 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // brought to it once at the end.
 constexpr float kLazy = 8.0f;
 
+// Per-workgroup constants of the key loop.
+template <typename T>
+struct LoopCtx {
+  const T* kbase;
+  const T* vbase;
+  const T* krbase;
+  int64_t krow_b, vrow_b, krrow_b;  // row strides in bytes
+  const uint8_t* mrow;              // this lane's mask row (edge blocks)
+  int skv, row, i0, last_row;
+  int lane, wave, l32, hh;
+  bool row_ok;
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes at
+// base + voff land at dst + 16 l.  The scalar buffer descriptor covers
+// [base, base + nbytes); lanes whose offset falls outside write zeros.
+__device__ __forceinline__ void dma16(const void* base, int64_t nbytes, lds_void* dst, uint32_t voff) {
+  const int n = (int)(nbytes < 0x7fffffff ? nbytes : 0x7fffffff);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000), dst, 16, voff, 0, 0, 0);
+}
+
+// Global -> LDS staging of the key block at row jb into stage `st`.  Scalar
+// buffer descriptors based at the block's first row and sized to the rows
+// left in the sequence make rows past the end arrive as zeros with no branch.
+// Load n of wave w fills LDS units [64 (4n + w), +64): lane l writes unit
+// 64 (4n + w) + l, i.e. row unit / U at physical unit unit % U, which holds the
+// logical unit the swizzle maps there.
+template <typename T, int D, int DR>
+__device__ __forceinline__ void stage_block(char* __restrict__ st, int jb, const LoopCtx<T>& x) {
+  using C = MfmaCfg<T, D, DR>;
+  const int64_t rows = min(x.skv - jb, C::BN);  // >= 1 for every visited block
+  const T* kb = x.kbase + (int64_t)jb * (x.krow_b / (int64_t)sizeof(T));
+#pragma unroll
+  for (int n = 0; n < C::K_LOADS; ++n) {
+    const int unit = 64 * (4 * n + x.wave) + x.lane;
+    const int r = unit / C::KU, u = k_swz(r, unit % C::KU);
+    dma16(kb, rows * x.krow_b, (lds_void*)(st + 1024 * (4 * n + x.wave)), (uint32_t)(r * x.krow_b + u * 16));
+  }
+  if constexpr (DR > 0) {
+    const T* krb = x.krbase + (int64_t)jb * (x.krrow_b / (int64_t)sizeof(T));
+#pragma unroll
+    for (int n = 0; n < C::KR_LOADS; ++n) {
+      const int unit = 64 * (4 * n + x.wave) + x.lane;
+      const int r = unit / C::KRU, u = k_swz(r, unit % C::KRU);
+      dma16(krb, rows * x.krrow_b, (lds_void*)(st + C::KR_OFF + 1024 * (4 * n + x.wave)),
+            (uint32_t)(r * x.krrow_b + u * 16));
+    }
+  }
+  const T* vb = x.vbase + (int64_t)jb * (x.vrow_b / (int64_t)sizeof(T));
+#pragma unroll
+  for (int n = 0; n < C::V_LOADS; ++n) {
+    const int unit = 64 * (4 * n + x.wave) + x.lane;
+    const int r = unit / C::VU, u = v_swz<C::VU>(r, unit % C::VU);
+    dma16(vb, rows * x.vrow_b, (lds_void*)(st + C::V_OFF + 1024 * (4 * n + x.wave)), (uint32_t)(r * x.vrow_b + u * 16));
+  }
+}
+
+// Whether the block at jb needs per-element tests (window edge, sequence end)
+// and whether it reads the mask.
+struct BlockKind {
+  bool partial, read_mask;
+};
+__device__ __forceinline__ BlockKind block_kind(const Params& p, int jb, int skv, int first_row, int last_row) {
+  const bool tail = jb + kMfmaBN > skv;
+  const bool edge = p.band && !(jb >= last_row - p.pre && jb + kMfmaBN - 1 <= first_row + p.next);
+  const bool rm = p.has_mask && (p.mask_everywhere || edge || tail);
+  return {tail || edge || rm, rm};
+}
+
+// Mask bytes of this lane's row for keys jb + 32t + 8a + 4hh + 0..3, word 4t + a
+// (nonzero byte = excluded).
+template <typename T>
+__device__ __forceinline__ void fetch_mask(uint32_t (&mw)[8], const Params& p, int jb, const LoopCtx<T>& x) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int key = jb + 32 * (w >> 2) + 8 * (w & 3) + 4 * x.hh;
+    if (p.mask_vec4) {
+      mw[w] = (x.row_ok && key < x.skv) ? *reinterpret_cast<const uint32_t*>(x.mrow + key) : 0u;
+    } else {
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        uint32_t byte = 0;
+        if (x.mrow != nullptr && key + b < x.skv && (!p.varlen || key + b < p.m_cols))
+          byte = x.mrow[(int64_t)(key + b) * p.m_sk];
+        else if (p.varlen)
+          byte = 1;  // outside the 2-D mask: excluded
+        v |= (byte ? 0xffu : 0u) << (8 * b);
+      }
+      mw[w] = v;
+    }
+  }
+}
+
+// One key block: prefetch the next block (and its mask words) into `nxt`,
+// then the scores from `cur`, the softmax step and the output update.  The
+// two stage pointers are restrict-qualified so the compiler knows the LDS
+// reads of `cur` do not depend on the loads in flight into `nxt`.  `mw` holds
+// this block's mask words on entry (fetched one block ahead) and the next
+// block's on exit.
+//
+// Excluded positions are applied before the score product: the accumulators
+// start at 0 for kept and -inf for excluded elements, and the MFMA adds K Q^T
+// to them (-inf + finite = -inf).  Nothing branches after the scores.
+template <typename T, int D, int DR>
+__device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __restrict__ nxt, int jb, bool more,
+                                          const Params& p, const LoopCtx<T>& x,
+                                          const typename Vec8<T>::type (&qf)[MfmaCfg<T, D, DR>::NKS],
+                                          f32x16 (&oacc)[MfmaCfg<T, D, DR>::NDT], float& m_ref, float& m_max,
+                                          float& lsum, uint32_t (&mw)[8]) {
+  using C = MfmaCfg<T, D, DR>;
+  using V8 = typename Vec8<T>::type;
+  constexpr int BN = C::BN;
+  const int l32 = x.l32, hh = x.hh, row = x.row;
+  const float c = p.scale_log2;
+
+  f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  const BlockKind bk = block_kind(p, jb, x.skv, x.i0, x.last_row);
+  if (bk.partial) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = jb + 32 * t + 8 * (j >> 2) + 4 * hh + (j & 3);
+        bool k_ok = key < x.skv;
+        if (p.band) k_ok = k_ok && (key - row <= p.next) && (row - key <= p.pre);
+        if (bk.read_mask) k_ok = k_ok && ((mw[4 * t + (j >> 2)] >> (8 * (j & 3))) & 0xffu) == 0;
+        sacc[t][j] = k_ok ? 0.f : kNegInf;
+      }
+    }
+  }
+
+  if (more) {
+    stage_block<T, D, DR>(nxt, jb + BN, x);
+    if (block_kind(p, jb + BN, x.skv, x.i0, x.last_row).read_mask) fetch_mask(mw, p, jb + BN, x);
+  }
+
+  // ---- S^T = K Q^T (+ the exclusion bias) for 64 keys x 32 rows: two 32x32 tiles
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r = 32 * t + l32;
+      const char* src = ks < D / 16 ? cur + (r * C::KU + k_swz(r, 2 * ks + hh)) * 16
+                                    : cur + C::KR_OFF + (r * C::KRU + k_swz(r, 2 * (ks - D / 16) + hh)) * 16;
+      const V8 a = *reinterpret_cast<const V8*>(src);
+      sacc[t] = mfma32<T>(a, qf[ks], sacc[t]);
+    }
+  }
+
+  // ---- online softmax (per lane: one query row, 32 of the block's keys)
+  float mx = kNegInf;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = __builtin_fmaxf(mx, sacc[t][j]);
+  mx = xhalf_max(mx);
+  const float mxc = mx * c;  // c > 0, so -inf stays -inf
+  m_max = __builtin_fmaxf(m_max, mxc);
+  if (mxc > m_ref + kLazy) {
+    const float alpha = fast_exp2(m_ref - mxc);  // 0 when m_ref = -inf
+    lsum *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] *= alpha;
+    m_ref = mxc;
+  }
+  const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+
+  V8 pk[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float e = fast_exp2(fmaf(sacc[t][j], c, -m_use));
+      lsum += e;
+      pk[t][j >> 3][j & 7] = from_f32<T>(e);
+    }
+
+  // ---- O^T += V^T P^T.  V^T operand: lane group q = lane / 16 covers output
+  // columns 32 dt + 16 (q & 1) + 0..15 and keys kb = 32 t + 16 s2 + 4 (q >> 1)
+  // (+8 for the second read); lane j of the group points at row kb + j / 4,
+  // columns 4 (j % 4) .. +3 of that 16-column span.
+  const int vq = x.lane >> 4, vj = x.lane & 15;
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) {
+    const int vu = 4 * dt + 2 * (vq & 1) + ((vj & 3) >> 1);  // logical unit of this lane's 4 columns
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int r0 = 32 * t + 16 * s2 + 4 * (vq >> 1) + (vj >> 2);
+        const int r1 = r0 + 8;
+        const char* a0 = cur + C::V_OFF + (r0 * C::VU + v_swz<C::VU>(r0, vu)) * 16 + 8 * (vj & 1);
+        const char* a1 = cur + C::V_OFF + (r1 * C::VU + v_swz<C::VU>(r1, vu)) * 16 + 8 * (vj & 1);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
+        const V8 a = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[dt] = mfma32<T>(a, pk[t][s2], oacc[dt]);
+      }
+    }
+  }
+}
+
 template <typename T, int D, int DR>
 __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   using C = MfmaCfg<T, D, DR>;
   using V8 = typename Vec8<T>::type;
   constexpr int BM = C::BM, BN = C::BN;
-  __shared__ __attribute__((aligned(16))) T smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
 
   const Tile tl = map_tile(p, blockIdx.x);
   if (!tl.valid) return;
@@ -128,7 +353,6 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   const int nblocks = (kv_hi >= kv_lo && last_row >= i0) ? (kv_hi - jb0) / BN + 1 : 0;
 
   // ---- running state, log2 domain: t = s * c, c = scale * log2(e)
-  const float c = p.scale_log2;
   float m_ref = kNegInf;  // reference max of the exponentials
   float m_max = kNegInf;  // true running max (for softmaxMax)
   float lsum = 0.f;       // this half-wave's part of sum_j 2^(t_j - m_ref)
@@ -143,221 +367,45 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] = f32x16{};
 
-  // ---- global -> register staging of one key block.  Buffer loads: each
-  // block gets a scalar descriptor based at its first row whose size covers
-  // only the rows left in the sequence, so rows past the end read as zero with
-  // no branch; the per-lane byte offsets are fixed for the whole loop.
-  const T* kbase = static_cast<const T*>(p.k) + tl.b * p.k_sb + g * p.k_sh + tl.kv_row0 * p.k_ss;
-  const T* vbase = static_cast<const T*>(p.v) + tl.b * p.v_sb + g * p.v_sh + tl.kv_row0 * p.v_ss;
-  const T* krbase =
-      DR ? static_cast<const T*>(p.kr) + tl.b * p.kr_sb + g * p.kr_sh + tl.kv_row0 * p.kr_ss : nullptr;
-  const int64_t krow_b = p.k_ss * (int64_t)sizeof(T), vrow_b = p.v_ss * (int64_t)sizeof(T);
-  const int64_t krrow_b = DR ? p.kr_ss * (int64_t)sizeof(T) : 0;
-  uint32_t kvoff[C::KCH], kloff[C::KCH];    // K: global byte offset in the block, LDS element offset
-  uint32_t krvoff[C::KRCH + 1], krloff[C::KRCH + 1];
-#pragma unroll
-  for (int i = 0; i < C::KCH; ++i) {
-    const int ch = tid + i * kMfmaThreads;
-    const int key = ch / (D / 8), col = ch % (D / 8);
-    kvoff[i] = (uint32_t)(key * krow_b + col * 16);
-    kloff[i] = key * C::KS + col * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < C::KRCH; ++i) {
-    const int ch = tid + i * kMfmaThreads;
-    const int key = ch / (DR / 8), col = ch % (DR / 8);
-    krvoff[i] = (uint32_t)(key * krrow_b + col * 16);
-    krloff[i] = key * C::KS + D + col * 8;
-  }
-  const int vkg = tid & 15, vdg = tid >> 4;  // V: keys 4*vkg..+3, dims 8*vdg..+7
-  const bool v_active = tid < C::VBLOCKS;
-  uint32_t vvoff[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) vvoff[r] = (uint32_t)((4 * vkg + r) * vrow_b + 16 * vdg);
-  const int voff = C::K_ELEMS + (8 * vdg) * C::VS + vt_pos(4 * vkg);
-
-  auto rsrc = [](const void* base, int64_t bytes) {
-    const int n = (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-  };
-  uint4 kreg[C::KCH];
-  uint4 krreg[C::KRCH + 1];
-  uint4 vreg[4];
-  auto load_block = [&](int jb) {
-    const int64_t rows = min(tl.skv - jb, BN);  // >= 1 for every visited block
-    const auto rk = rsrc(kbase + (int64_t)jb * p.k_ss, rows * krow_b);
-#pragma unroll
-    for (int i = 0; i < C::KCH; ++i)
-      kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, kvoff[i], 0, 0));
-    if constexpr (DR > 0) {
-      const auto rkr = rsrc(krbase + (int64_t)jb * p.kr_ss, rows * krrow_b);
-#pragma unroll
-      for (int i = 0; i < C::KRCH; ++i)
-        krreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rkr, krvoff[i], 0, 0));
-    }
-    if (v_active) {
-      const auto rv = rsrc(vbase + (int64_t)jb * p.v_ss, rows * vrow_b);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vvoff[r], 0, 0));
-    }
-  };
-  auto store_block = [&](int stage) {
-    T* st = smem + stage * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::KCH; ++i) *reinterpret_cast<uint4*>(st + kloff[i]) = kreg[i];
-#pragma unroll
-    for (int i = 0; i < C::KRCH; ++i) *reinterpret_cast<uint4*>(st + krloff[i]) = krreg[i];
-    if (v_active) {
-      // 4 keys x 8 dims -> 8 dims x 4 keys (pairs of 16-bit lanes regrouped)
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        uint32_t lo, hi;
-        if (e & 1) {
-          lo = (w0[w] >> 16) | (w1[w] & 0xffff0000u);
-          hi = (w2[w] >> 16) | (w3[w] & 0xffff0000u);
-        } else {
-          lo = (w0[w] & 0xffffu) | (w1[w] << 16);
-          hi = (w2[w] & 0xffffu) | (w3[w] << 16);
-        }
-        *reinterpret_cast<uint2*>(st + voff + e * C::VS) = make_uint2(lo, hi);
-      }
-    }
-  };
-
-  // mask row of this lane (dense: [b|0, h|0, row, :]; TND: the 2-D mask in local coordinates)
-  const uint8_t* mrow = nullptr;
-  if (p.has_mask) {
+  LoopCtx<T> x;
+  x.kbase = static_cast<const T*>(p.k) + tl.b * p.k_sb + g * p.k_sh + tl.kv_row0 * p.k_ss;
+  x.vbase = static_cast<const T*>(p.v) + tl.b * p.v_sb + g * p.v_sh + tl.kv_row0 * p.v_ss;
+  x.krbase = DR ? static_cast<const T*>(p.kr) + tl.b * p.kr_sb + g * p.kr_sh + tl.kv_row0 * p.kr_ss : nullptr;
+  x.krow_b = p.k_ss * (int64_t)sizeof(T);
+  x.vrow_b = p.v_ss * (int64_t)sizeof(T);
+  x.krrow_b = DR ? p.kr_ss * (int64_t)sizeof(T) : 0;
+  x.mrow = nullptr;
+  if (p.has_mask) {  // dense: [b|0, h|0, row, :]; TND: the 2-D mask in local coordinates
     if (p.varlen)
-      mrow = row < p.m_rows ? p.mask + (int64_t)row * p.m_sq : nullptr;
+      x.mrow = row < p.m_rows ? p.mask + (int64_t)row * p.m_sq : nullptr;
     else
-      mrow = p.mask + tl.b * p.m_sb + tl.h * p.m_sh + (int64_t)(row_ok ? row : 0) * p.m_sq;
+      x.mrow = p.mask + tl.b * p.m_sb + tl.h * p.m_sh + (int64_t)(row_ok ? row : 0) * p.m_sq;
   }
+  x.skv = tl.skv;
+  x.row = row;
+  x.i0 = i0;
+  x.last_row = last_row;
+  x.lane = lane;
+  x.wave = wave;
+  x.l32 = l32;
+  x.hh = hh;
+  x.row_ok = row_ok;
 
+  uint32_t mw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (nblocks > 0) {
-    load_block(jb0);
-    store_block(0);
+    stage_block<T, D, DR>(smem, jb0, x);
+    if (block_kind(p, jb0, x.skv, x.i0, x.last_row).read_mask) fetch_mask(mw, p, jb0, x);
   }
-  // Wait here once for the Q fragments (and the first block): otherwise the
-  // compiler cannot prove they landed and re-waits for every outstanding load,
-  // including the next block's prefetch, at the top of each iteration.
+  // Wait here once for the Q fragments, the first block and its mask words.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   __syncthreads();
 
   for (int it = 0; it < nblocks; ++it) {
-    const int jb = jb0 + it * BN;
     const int stg = it & 1;
-    const bool more = it + 1 < nblocks;
-
-    // ---- blocks crossing the window edge or the sequence end, or needing the
-    // mask, test each element.  Mask bytes are fetched first so that waiting
-    // for them does not also wait for the next block's prefetch.
-    const bool tail = jb + BN > tl.skv;
-    const bool edge = p.band && !(jb >= last_row - p.pre && jb + BN - 1 <= i0 + p.next);
-    const bool read_mask = p.has_mask && (p.mask_everywhere || edge || tail);
-    uint32_t mw[8];  // mask bytes of keys jb + 32t + 8a + 4hh + 0..3, word 4t + a
-    if (read_mask) {
-      if (p.mask_vec4) {
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int key = jb + 32 * (w >> 2) + 8 * (w & 3) + 4 * hh;
-          mw[w] = (row_ok && key < tl.skv) ? *reinterpret_cast<const uint32_t*>(mrow + key) : 0u;
-        }
-      } else {
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          uint32_t v = 0;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int key = jb + 32 * (w >> 2) + 8 * (w & 3) + 4 * hh + b;
-            uint32_t byte = 0;
-            if (mrow != nullptr && key < tl.skv && (!p.varlen || key < p.m_cols)) byte = mrow[(int64_t)key * p.m_sk];
-            else if (p.varlen) byte = 1;  // outside the 2-D mask: excluded
-            v |= (byte ? 0xffu : 0u) << (8 * b);
-          }
-          mw[w] = v;
-        }
-      }
-    }
-
-    if (more) load_block(jb + BN);
-
-    const T* ks_ = smem + stg * C::STAGE;
-    const T* vs_ = ks_ + C::K_ELEMS;
-
-    // ---- S^T = K Q^T for 64 keys x 32 rows: two 32x32 tiles
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const V8 a = *reinterpret_cast<const V8*>(ks_ + (32 * t + l32) * C::KS + 16 * ks + 8 * hh);
-        sacc[t] = mfma32<T>(a, qf[ks], sacc[t]);
-      }
-    }
-
-    // excluded scores become -inf (weight exactly 0 below)
-    if (tail || edge || read_mask) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = jb + 32 * t + 8 * (j >> 2) + 4 * hh + (j & 3);
-          bool k_ok = key < tl.skv;
-          if (p.band) k_ok = k_ok && (key - row <= p.next) && (row - key <= p.pre);
-          if (read_mask) k_ok = k_ok && ((mw[4 * t + (j >> 2)] >> (8 * (j & 3))) & 0xffu) == 0;
-          sacc[t][j] = k_ok ? sacc[t][j] : kNegInf;
-        }
-      }
-    }
-
-    // ---- online softmax (per lane: one query row, 32 of the block's keys)
-    float mx = kNegInf;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = __builtin_fmaxf(mx, sacc[t][j]);
-    mx = xhalf_max(mx);
-    const float mxc = mx * c;  // c > 0, so -inf stays -inf
-    m_max = __builtin_fmaxf(m_max, mxc);
-    if (mxc > m_ref + kLazy) {
-      const float alpha = fast_exp2(m_ref - mxc);  // 0 when m_ref = -inf
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] *= alpha;
-      m_ref = mxc;
-    }
-    const float m_use = m_ref == kNegInf ? 0.f : m_ref;
-
-    V8 pk[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float e = fast_exp2(fmaf(sacc[t][j], c, -m_use));
-        lsum += e;
-        pk[t][j >> 3][j & 7] = from_f32<T>(e);
-      }
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const V8 a = *reinterpret_cast<const V8*>(vs_ + (32 * dt + l32) * C::VS + 32 * t + 16 * s2 + 8 * hh);
-          oacc[dt] = mfma32<T>(a, pk[t][s2], oacc[dt]);
-        }
-      }
-    }
-
-    if (more) store_block(stg ^ 1);
+    key_block<T, D, DR>(smem + stg * C::STAGE_BYTES, smem + (stg ^ 1) * C::STAGE_BYTES, jb0 + it * BN,
+                        it + 1 < nblocks, p, x, qf, oacc, m_ref, m_max, lsum, mw);
+    // this thread's loads of the next block landed; then everyone's, before the swap
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
   }
 

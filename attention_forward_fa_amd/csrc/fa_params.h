@@ -8,14 +8,18 @@ namespace fa {
 
 // Which kernel family a plan launches.
 enum KernelKind : int32_t {
-  KERNEL_MFMA = 0,    // bf16/fp16, MFMA 32x32x16, D in {64,128}, Dr in {0,64}, Dv == D
-  KERNEL_GENERIC = 1, // any dtype, one query row per lane, fp32 VALU dot products
+  KERNEL_MFMA = 0,     // bf16/fp16, MFMA 32x32x16, 4 waves, D in {64,128}, Dr in {0,64}, Dv == D
+  KERNEL_GENERIC = 1,  // any dtype, one query row per lane, fp32 VALU dot products
+  KERNEL_MFMA_PP = 2,  // as KERNEL_MFMA with 8 waves in two anti-phase groups (BM = 256)
 };
 
 // Tile of the MFMA kernel: 4 wavefronts x 32 query rows, 64 keys per step.
 constexpr int kMfmaBM = 128;
 constexpr int kMfmaBN = 64;
 constexpr int kMfmaThreads = 256;
+// Tile of the two-group matrix-core kernel: 8 wavefronts, 256 query rows.
+constexpr int kMfmaPpBM = 256;
+constexpr int kMfmaPpThreads = 512;
 // Tile of the generic kernel: one wavefront, one query row per lane.
 constexpr int kGenericBM = 64;
 constexpr int kGenericBN = 32;

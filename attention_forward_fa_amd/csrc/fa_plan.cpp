@@ -9,6 +9,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <stdlib.h>
+
 #include <new>
 
 #include "fa_fwd.h"
@@ -133,7 +135,8 @@ extern "C" int32_t fa_plan_describe(const fa_plan* plan, char* buf, size_t len) 
                          "kernel=%s dtype=%s d=%d dr=%d dv=%d bm=%d bn=%d grid=%d block=%d ws=%llu "
                          "varlen=%d band=%d pre=%d next=%d mask=%d mask_everywhere=%d sink=%d "
                          "nq=%d nkv=%d tiles_per_head=%d reverse=%d",
-                         plan->kind == fa::KERNEL_MFMA ? "mfma" : "generic", dtype_name(plan->dtype), p.d, p.dr,
+                         plan->kind == fa::KERNEL_MFMA_PP ? "mfma_pp" : (plan->kind == fa::KERNEL_MFMA ? "mfma" : "generic"),
+                         dtype_name(plan->dtype), p.d, p.dr,
                          p.dv, plan->bm, plan->bn, p.num_wg, plan->block, (unsigned long long)plan->ws_bytes,
                          p.varlen, p.band, p.pre, p.next, p.has_mask, p.mask_everywhere, p.has_sink, p.nq, p.nkv,
                          p.tiles_per_head, p.reverse_tiles);
@@ -314,10 +317,31 @@ extern "C" fa_status fa_fwd_get_workspace_size(
                        (dr == 0 || dr == 64) && vec_ok(query->data, q) && vec_ok(key->data, k) &&
                        vec_ok(value->data, v) && vec_ok(attention_out->data, o) &&
                        (!query_rope || (vec_ok(query_rope->data, qr) && vec_ok(key_rope->data, kr))) && stats_vec;
-  pl->kind = mfma_ok ? fa::KERNEL_MFMA : fa::KERNEL_GENERIC;
-  pl->bm = mfma_ok ? fa::kMfmaBM : fa::kGenericBM;
-  pl->bn = mfma_ok ? fa::kMfmaBN : fa::kGenericBN;
-  pl->block = mfma_ok ? fa::kMfmaThreads : fa::kGenericThreads;
+  // Family: the four-wave matrix-core kernel wherever it applies (it measures
+  // faster than the two-group kernel on every workload here), the generic
+  // kernel for everything else.  FA_FWD_KERNEL=mfma|pp|generic forces a family
+  // (tests and benchmarks); forcing a matrix-core family on a shape it does not
+  // cover is an error.
+  int kind = mfma_ok ? fa::KERNEL_MFMA : fa::KERNEL_GENERIC;
+  if (const char* force = getenv("FA_FWD_KERNEL")) {
+    if (!strcmp(force, "generic")) {
+      kind = fa::KERNEL_GENERIC;
+    } else if (!strcmp(force, "mfma") || !strcmp(force, "pp")) {
+      if (!mfma_ok) {
+        delete pl;
+        return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL=%s: shape, dtype or alignment not covered", force);
+      }
+      kind = !strcmp(force, "pp") ? fa::KERNEL_MFMA_PP : fa::KERNEL_MFMA;
+    } else if (force[0] != '\0') {
+      delete pl;
+      return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL='%s' not one of pp, mfma, generic", force);
+    }
+  }
+  pl->kind = kind;
+  pl->bm = kind == fa::KERNEL_MFMA_PP ? fa::kMfmaPpBM : (kind == fa::KERNEL_MFMA ? fa::kMfmaBM : fa::kGenericBM);
+  pl->bn = kind == fa::KERNEL_GENERIC ? fa::kGenericBN : fa::kMfmaBN;
+  pl->block = kind == fa::KERNEL_MFMA_PP ? fa::kMfmaPpThreads
+                                         : (kind == fa::KERNEL_MFMA ? fa::kMfmaThreads : fa::kGenericThreads);
 
   p.q = query->data; p.k = key->data; p.v = value->data;
   p.qr = query_rope ? query_rope->data : nullptr;

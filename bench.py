@@ -33,8 +33,8 @@ METRIC = "attention fwd TFLOP/s + % of MI355X bf16 MFMA peak, B2 S4096 N24 D128"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 HBM_GBPS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
-KERNEL_SOURCES = ["fa_mfma.hpp", "fa_device.hpp", "fa_params.h", "fa_mfma_bf16.hip", "fa_mfma_f16.hip",
-                  "fa_generic.hip", "fa_launch.hip"]
+KERNEL_SOURCES = ["fa_mfma.hpp", "fa_mfma_pp.hpp", "fa_device.hpp", "fa_params.h", "fa_mfma_bf16.hip",
+                  "fa_mfma_f16.hip", "fa_generic.hip", "fa_launch.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -307,7 +307,7 @@ def main():
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic},
-        "kernel": {"name": "fa_fwd_mfma" if "kernel=mfma" in desc else "fa_fwd_generic", "plan": desc,
+        "kernel": {"name": "fa_fwd_" + desc.split()[0].split("=")[1], "plan": desc,
                    "avg_ms": round(kernel_ms_avg, 5), "median_ms": round(kernel_ms_med, 5),
                    "flops_per_launch": flops, "flops_exact_pairs": pairs_exact * fpp,
                    "algorithmic_bytes_per_launch": abytes,

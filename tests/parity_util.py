@@ -11,7 +11,9 @@ Tolerances (written here, used by every parity test):
 """
 from __future__ import annotations
 
+import contextlib
 import math
+import os
 from typing import Dict, Optional
 
 import torch
@@ -19,6 +21,23 @@ import torch
 import synth
 from attention_forward_fa_amd import api
 from oracle import attention as orc
+
+
+@contextlib.contextmanager
+def forced_kernel(kind: str):
+    """Force the library's kernel family (FA_FWD_KERNEL) for the calls inside; 'auto' = the plan's choice."""
+    old = os.environ.get("FA_FWD_KERNEL")
+    if kind == "auto":
+        os.environ.pop("FA_FWD_KERNEL", None)
+    else:
+        os.environ["FA_FWD_KERNEL"] = kind
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("FA_FWD_KERNEL", None)
+        else:
+            os.environ["FA_FWD_KERNEL"] = old
 
 
 def to_gpu(t: Optional[torch.Tensor], dev="cuda:0"):

@@ -87,7 +87,7 @@ def test_dense_headline_plan():
     try:
         assert ws == 0
         d = describe(pl)
-        assert "kernel=mfma" in d and "grid=1536" in d and "dtype=bf16" in d, d
+        assert "kernel=mfma " in d and "grid=1536" in d and "block=256" in d and "dtype=bf16" in d, d
     finally:
         _lib.fa_plan_destroy(pl)
 
@@ -101,7 +101,7 @@ def test_varlen_plan_workspace():
     assert st == 0, _lib.last_error_message()
     assert ws == 4 * 17
     d = describe(pl)
-    assert "varlen=1" in d and "grid=1920" in d and "reverse=1" in d, d  # (64 + 16) tiles x 24 heads
+    assert "varlen=1" in d and "grid=1920" in d and "reverse=1" in d, d  # (64 + 16) 128-row tiles x 24 heads
     _lib.fa_plan_destroy(pl)
 
 
@@ -326,3 +326,36 @@ def test_describe_truncates_safely():
     n = L.fa_plan_describe(pl, buf, 8)
     assert n > 8 and len(buf.value) == 7
     _lib.fa_plan_destroy(pl)
+
+
+def test_small_grid_uses_four_wave_kernel():
+    s = [1, 300, 2, 128]
+    st, ws, pl = plan(desc(s), desc(s), desc(s), desc(s))
+    assert st == 0
+    d = describe(pl)
+    assert "kernel=mfma " in d and "bm=128" in d and "grid=6" in d, d
+    _lib.fa_plan_destroy(pl)
+
+
+@pytest.mark.parametrize("force,expect", [("mfma", "kernel=mfma grid=1536"), ("pp", "kernel=mfma_pp grid=768"),
+                                          ("generic", "kernel=generic"), ("", "kernel=mfma grid=1536")])
+def test_forced_kernel_family(monkeypatch, force, expect):
+    monkeypatch.setenv("FA_FWD_KERNEL", force)
+    q, k, v, o = c2()
+    st, ws, pl = plan(q, k, v, o)
+    assert st == 0, _lib.last_error_message()
+    d = describe(pl)
+    for part in expect.split():
+        assert part in d.split(), d
+    _lib.fa_plan_destroy(pl)
+
+
+def test_forced_kernel_errors(monkeypatch):
+    monkeypatch.setenv("FA_FWD_KERNEL", "mfma")
+    s = [1, 2, 128, 64]
+    st, _, pl = plan(desc(s, F32), desc(s, F32), desc(s, F32), desc(s, F32), layout=b"BNSD")
+    assert st == 561103 and pl is None and "FA_FWD_KERNEL" in _lib.last_error_message()
+    monkeypatch.setenv("FA_FWD_KERNEL", "fastest")
+    q, k, v, o = c2()
+    st, _, pl = plan(q, k, v, o)
+    assert st == 561103 and pl is None

@@ -106,11 +106,23 @@ def _sink_neg_inf_case(seed):
     return c
 
 
+KERNELS = ["auto", "mfma", "pp", "generic"]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_small_case(name):
+def test_small_case(name, kernel):
     case = SMALL[name]()
-    print(f"[parity] start {name} layout={case.layout} q={tuple(case.q.shape)} dtype={case.q.dtype}", flush=True)
-    _report(name, pu.compare_case(case))
+    print(f"[parity] start {name} kernel={kernel} layout={case.layout} q={tuple(case.q.shape)} dtype={case.q.dtype}",
+          flush=True)
+    with pu.forced_kernel(kernel):
+        try:
+            errs = pu.compare_case(case)
+        except _lib.FaError as e:
+            if kernel != "auto" and e.code == _lib.FA_ERR_UNSUPPORTED and "FA_FWD_KERNEL" in e.message:
+                pytest.skip(f"{kernel} does not cover this case")
+            raise
+    _report(f"{name}/{kernel}", errs)
 
 
 @pytest.mark.parametrize("layout", ["BSH", "SBH"])
@@ -160,11 +172,13 @@ def test_misaligned_uses_generic_and_matches():
 # determinism, guard bands, repeated plan execution
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("kernel", ["mfma", "pp"])
 @pytest.mark.parametrize("name", ["c2_small_bf16", "c4_small_varlen", "c5_small_sink_rope"])
-def test_bitwise_deterministic(name):
+def test_bitwise_deterministic(name, kernel):
     case = SMALL[name]()
-    a = pu.run_gpu(case)
-    b = pu.run_gpu(case)
+    with pu.forced_kernel(kernel):
+        a = pu.run_gpu(case)
+        b = pu.run_gpu(case)
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.uint8) if x.dtype != torch.float32 else x.view(torch.int32),
                            y.view(torch.uint8) if y.dtype != torch.float32 else y.view(torch.int32))
@@ -247,7 +261,8 @@ def _full_case(name):
 def test_full_size_sampled(name):
     case = _full_case(name)
     print(f"[parity] full {name} q={tuple(case.q.shape)}", flush=True)
-    o, smax, ssum = pu.run_gpu(case)
+    with pu.forced_kernel("auto"):
+        o, smax, ssum = pu.run_gpu(case)
     g = synth.generator(999)
     if case.layout == "TND":
         cu = case.cu_seqlens_q.tolist()
