@@ -220,19 +220,38 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
   const int l32 = x.l32, hh = x.hh, row = x.row;
   const float c = p.scale_log2;
 
-  f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  // ---- S^T = K Q^T (+ the exclusion bias) for 64 keys x 32 rows: two 32x32
+  // tiles.  Only the first k-step differs between edge and full blocks (bias
+  // or zero as the initial accumulator); it runs before the prefetch so the
+  // mask words are consumed before the next block's overwrite them.
+  auto kfrag = [&](int ks, int t) {
+    const int r = 32 * t + l32;
+    const char* src = ks < D / 16 ? cur + (r * C::KU + k_swz(r, 2 * ks + hh)) * 16
+                                  : cur + C::KR_OFF + (r * C::KRU + k_swz(r, 2 * (ks - D / 16) + hh)) * 16;
+    return *reinterpret_cast<const V8*>(src);
+  };
   const BlockKind bk = block_kind(p, jb, x.skv, x.i0, x.last_row);
-  if (bk.partial) {
+  f32x16 sacc[2];
+  {
+    const V8 a0 = kfrag(0, 0), a1 = kfrag(0, 1);
+    if (bk.partial) {
+      f32x16 bias[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = jb + 32 * t + 8 * (j >> 2) + 4 * hh + (j & 3);
-        bool k_ok = key < x.skv;
-        if (p.band) k_ok = k_ok && (key - row <= p.next) && (row - key <= p.pre);
-        if (bk.read_mask) k_ok = k_ok && ((mw[4 * t + (j >> 2)] >> (8 * (j & 3))) & 0xffu) == 0;
-        sacc[t][j] = k_ok ? 0.f : kNegInf;
+        for (int j = 0; j < 16; ++j) {
+          const int key = jb + 32 * t + 8 * (j >> 2) + 4 * hh + (j & 3);
+          bool k_ok = key < x.skv;
+          if (p.band) k_ok = k_ok && (key - row <= p.next) && (row - key <= p.pre);
+          if (bk.read_mask) k_ok = k_ok && ((mw[4 * t + (j >> 2)] >> (8 * (j & 3))) & 0xffu) == 0;
+          bias[t][j] = k_ok ? 0.f : kNegInf;
+        }
       }
+      sacc[0] = mfma32<T>(a0, qf[0], bias[0]);
+      sacc[1] = mfma32<T>(a1, qf[0], bias[1]);
+    } else {
+      sacc[0] = mfma32<T>(a0, qf[0], f32x16{});
+      sacc[1] = mfma32<T>(a1, qf[0], f32x16{});
     }
   }
 
@@ -241,17 +260,10 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
     if (block_kind(p, jb + BN, x.skv, x.i0, x.last_row).read_mask) fetch_mask(mw, p, jb + BN, x);
   }
 
-  // ---- S^T = K Q^T (+ the exclusion bias) for 64 keys x 32 rows: two 32x32 tiles
 #pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) {
+  for (int ks = 1; ks < C::NKS; ++ks) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int r = 32 * t + l32;
-      const char* src = ks < D / 16 ? cur + (r * C::KU + k_swz(r, 2 * ks + hh)) * 16
-                                    : cur + C::KR_OFF + (r * C::KRU + k_swz(r, 2 * (ks - D / 16) + hh)) * 16;
-      const V8 a = *reinterpret_cast<const V8*>(src);
-      sacc[t] = mfma32<T>(a, qf[ks], sacc[t]);
-    }
+    for (int t = 0; t < 2; ++t) sacc[t] = mfma32<T>(kfrag(ks, t), qf[ks], sacc[t]);
   }
 
   // ---- online softmax (per lane: one query row, 32 of the block's keys)
