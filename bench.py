@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s + % of MI355X bf16 MFMA peak, B2 S4096 N24 D128"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 HBM_GBPS = 8000.0
-COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCES = ["fa_mfma.hpp", "fa_mfma_pp.hpp", "fa_device.hpp", "fa_params.h", "fa_mfma_bf16.hip",
                   "fa_mfma_f16.hip", "fa_generic.hip", "fa_launch.hip"]
 
@@ -125,15 +125,18 @@ def algorithmic_bytes(case) -> int:
 
 
 def load_traffic(src_hash: str, workload: str, dtype: str):
-    """HBM bytes per launch from committed rocprofv3 counters, if taken on this kernel source."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on this kernel source (else None)."""
     if not os.path.exists(COUNTERS):
         return None
     with open(COUNTERS) as f:
-        data = json.load(f)
-    rec = data.get(f"{workload}:{dtype}")
-    if not rec or rec.get("kernel_source_hash") != src_hash:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        for line in f:
+            parts = line.split()
+            if not parts or parts[0].startswith("#") or len(parts) < 6:
+                continue
+            if parts[0] == workload and parts[1] == dtype and parts[2] == src_hash:
+                return int(parts[5])
+    return None
 
 
 # ---------------------------------------------------------------------------
