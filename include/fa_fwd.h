@@ -137,6 +137,13 @@ typedef int32_t fa_status;
  *                       fa_plan_destroy().  It records the tensors' device
  *                       addresses; it may be executed any number of times.
  *
+ * Kernel choice: the matrix-core kernel when q is F16/BF16, D is 64 or 128,
+ * Dr is 0 or 64, Dv == D and every row start is 16-byte aligned; otherwise
+ * the generic one (fp32 dot products on the vector units).  The environment
+ * variable FA_FWD_KERNEL = "mfma" | "pp" | "generic", read here, forces a
+ * family for testing; forcing one the arguments do not fit returns
+ * FA_ERR_UNSUPPORTED.
+ *
  * Returns FA_OK, FA_ERR_PARAM_NULLPTR, FA_ERR_PARAM_INVALID or
  * FA_ERR_UNSUPPORTED.  On error *plan is set to NULL.  No device work.
  */
