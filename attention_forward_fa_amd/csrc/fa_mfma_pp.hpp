@@ -1,56 +1,339 @@
 // FlashAttention forward for bf16 / fp16 on gfx950: two wave groups in
 // anti-phase ("ping-pong").
 //
-// Same arithmetic as the four-wave kernel (fa_mfma.hpp: transposed products,
-// one query row per lane, lazy rescale, V^T in LDS with bits 2 and 3 of the key
-// swapped), re-timed so the matrix cores and the vector ALUs of a SIMD work at
-// the same time.  A workgroup has 8 wavefronts in two groups of 4; each group
-// owns 128 query rows (BM = 256).  Per key block k a group runs
+// Same arithmetic as the four-wave kernel (transposed products, one query row
+// per lane, lazy rescale, K and V staged straight into LDS, V^T read with the
+// transposing LDS load), re-timed so the matrix cores and the vector ALUs of a
+// SIMD work at the same time.  A workgroup has 8 wavefronts in two groups of
+// 4 (wave w is in group w / 4 and runs on SIMD w % 4, so every SIMD holds one
+// wave of each group); each group owns 128 query rows (BM = 256) and both
+// share the key / value stream, so every K / V byte staged into LDS serves
+// 256 query rows.  Per key block k a group runs
 //
-//   M phase: S_{k+1} = K_{k+1} Q^T   and   O += V_k P_k      (32 MFMA)
-//   V phase: P_{k+1} = softmax step of S_{k+1}               (VALU + exp)
+//   M phase: S_{k+1} = K_{k+1} Q^T   and   O += P_k V_k      (matrix cores)
+//   V phase: P_{k+1} = softmax step of S_{k+1}               (vector ALUs)
 //
 // and the groups are offset by one phase, with a workgroup barrier between
-// phases: while group 0 issues matrix instructions, group 1 (one wave on every
-// SIMD) does its softmax, then they swap.  Each SIMD therefore always has one
-// wave feeding the matrix core and one feeding the VALU.
+// phases: while group 0 issues matrix instructions, group 1 does its softmax,
+// then they swap.  The M phase runs at raised wave priority, and its LDS
+// operand reads are issued four MFMAs ahead of their use.
 //
-// Loads: group 0 stages K (and Krope) blocks, group 1 stages V blocks.  The
-// loads for K_{k+2} and V_{k+1} are issued in phase 2k and written to LDS in
-// phase 2k+1, into the buffers whose previous contents were last read in
-// phase 2k-1.  Mask bytes (edge blocks only) are read in the softmax step.
+// K and V: NSLOT slots, block b in slot b % NSLOT.  All 512 threads load
+// block b + NSLOT - 1 at the start of step b (phase 2b); a block is read for
+// the last time in phase 2b + 1, so its slot is free by then.  Every step
+// issues the same loads (past the last block they read zeros into a free
+// slot), and the end of each odd phase waits for all but the newest
+// NSLOT - 3 blocks, so block b + 2 is in LDS before phase 2b + 2.
+//
+// Masking (window edge, sequence end, explicit mask) is applied to the
+// scores in the softmax step of the blocks that need it.
 #pragma once
 
 #include "fa_mfma.hpp"
 
 namespace fa {
 
-// Position of key k inside a 64-key block of the transposed V tile (bits 2
-// and 3 swapped, so the keys of one MFMA k-step are one 16-byte read).
-__device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
-
-constexpr int kPpThreads = 512;
-constexpr int kPpBM = 256;
+constexpr int kPpThreads = kMfmaPpThreads;
+constexpr int kPpBM = kMfmaPpBM;
 
 template <typename T, int D, int DR>
 struct PpCfg {
   static constexpr int BN = kMfmaBN;
   static constexpr int DK = D + DR;
   static constexpr int DV = D;
-  static constexpr int KS = DK + 8;
-  static constexpr int VS = BN + 8;
-  static constexpr int K_ELEMS = BN * KS;
-  static constexpr int V_ELEMS = DV * VS;
-  static constexpr int KCH = BN * D / 8 / 256;    // K chunks per group-0 thread
-  static constexpr int KRCH = BN * DR / 8 / 256;  // Krope chunks per group-0 thread
-  static constexpr int VBLOCKS = (BN / 4) * (DV / 8);
+  static constexpr int KU = D / 8;    // 16-byte units per K row
+  static constexpr int KRU = DR / 8;  // units per Krope row
+  static constexpr int VU = DV / 8;   // units per V row
+  static constexpr int K_BYTES = BN * KU * 16;
+  static constexpr int KR_BYTES = BN * KRU * 16;
+  static constexpr int V_BYTES = BN * VU * 16;
+  static constexpr int KR_OFF = K_BYTES;  // offsets within a slot
+  static constexpr int V_OFF = K_BYTES + KR_BYTES;
+  static constexpr int SLOT = K_BYTES + KR_BYTES + V_BYTES;
+  static constexpr int NSLOT = 4 * SLOT <= 128 * 1024 ? 4 : 3;
+  static constexpr int LDS_BYTES = NSLOT * SLOT;
+  static constexpr int K_LOADS = BN * KU / kPpThreads;  // 16-byte loads per thread per block
+  static constexpr int KR_LOADS = BN * KRU / kPpThreads;
+  static constexpr int V_LOADS = BN * VU / kPpThreads;
+  static constexpr int LPB = K_LOADS + KR_LOADS + V_LOADS;
   static constexpr int NKS = DK / 16;
   static constexpr int NDT = DV / 32;
 };
 
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+template <typename T>
+struct PpCtx {
+  const T* kbase;
+  const T* vbase;
+  const T* krbase;
+  int64_t krow_b, vrow_b, krrow_b;
+  const uint8_t* mrow;  // this lane's mask row (blocks that read the mask)
+  int skv, row, g_first, g_last;
+  int lane, wave, l32, hh;
+  bool row_ok;
+};
+
+// Per-lane running state of one query row.
+template <typename T, int D, int DR>
+struct PpState {
+  typename Vec8<T>::type qf[PpCfg<T, D, DR>::NKS];  // Q^T fragments (B operand)
+  f32x16 oacc[PpCfg<T, D, DR>::NDT];              // O^T accumulator
+  f32x16 sacc[2];                                  // S^T of the block in flight
+  typename Vec8<T>::type pk[2][2];                 // P^T of the previous block
+  float m_ref, m_max, lsum;
+};
+
+// All 512 threads: K (+ Krope) and V of the block at jb into `slot`.  Load n
+// of wave w fills LDS units [64 (8n + w), +64) of each part; rows past the
+// sequence end (or a block past the last) read as zeros.
+template <typename T, int D, int DR>
+__device__ __forceinline__ void pp_stage(char* __restrict__ slot, int jb, const PpCtx<T>& x) {
+  using C = PpCfg<T, D, DR>;
+  jb = __builtin_amdgcn_readfirstlane(jb);  // uniform: the descriptors stay scalar
+  const int64_t rows = max(min(x.skv - jb, C::BN), 0);
+  const int64_t jbc = min(jb, x.skv);  // keeps the base inside the tensor
+  const T* kb = x.kbase + jbc * (x.krow_b / (int64_t)sizeof(T));
+#pragma unroll
+  for (int n = 0; n < C::K_LOADS; ++n) {
+    const int unit = 64 * (8 * n + x.wave) + x.lane;
+    const int r = unit / C::KU, u = k_swz(r, unit % C::KU);
+    dma16(kb, rows * x.krow_b, (lds_void*)(slot + 1024 * (8 * n + x.wave)), (uint32_t)(r * x.krow_b + u * 16));
+  }
+  if constexpr (DR > 0) {
+    const T* krb = x.krbase + jbc * (x.krrow_b / (int64_t)sizeof(T));
+#pragma unroll
+    for (int n = 0; n < C::KR_LOADS; ++n) {
+      const int unit = 64 * (8 * n + x.wave) + x.lane;
+      const int r = unit / C::KRU, u = k_swz(r, unit % C::KRU);
+      dma16(krb, rows * x.krrow_b, (lds_void*)(slot + C::KR_OFF + 1024 * (8 * n + x.wave)),
+            (uint32_t)(r * x.krrow_b + u * 16));
+    }
+  }
+  const T* vb = x.vbase + jbc * (x.vrow_b / (int64_t)sizeof(T));
+#pragma unroll
+  for (int n = 0; n < C::V_LOADS; ++n) {
+    const int unit = 64 * (8 * n + x.wave) + x.lane;
+    const int r = unit / C::VU, u = v_swz<C::VU>(r, unit % C::VU);
+    dma16(vb, rows * x.vrow_b, (lds_void*)(slot + C::V_OFF + 1024 * (8 * n + x.wave)),
+          (uint32_t)(r * x.vrow_b + u * 16));
+  }
+}
+
+// S^T = K Q^T for the block in `slot` (64 keys x this wave's 32 rows).
+template <typename T, int D, int DR>
+__device__ __forceinline__ void pp_scores(const char* __restrict__ slot, const PpCtx<T>& x,
+                                          const typename Vec8<T>::type (&qf)[PpCfg<T, D, DR>::NKS],
+                                          f32x16 (&s)[2]) {
+  using C = PpCfg<T, D, DR>;
+  using V8 = typename Vec8<T>::type;
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+#pragma unroll
+  for (int kstep = 0; kstep < C::NKS; ++kstep) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r = 32 * t + x.l32;
+      const char* src = kstep < D / 16
+                            ? slot + (r * C::KU + k_swz(r, 2 * kstep + x.hh)) * 16
+                            : slot + C::KR_OFF + (r * C::KRU + k_swz(r, 2 * (kstep - D / 16) + x.hh)) * 16;
+      s[t] = mfma32<T>(*reinterpret_cast<const V8*>(src), qf[kstep], s[t]);
+    }
+  }
+}
+
+// LDS operand reads run this many MFMAs ahead in the M phase.
+constexpr int kPpAhead = 4;
+
+// The M phase as one stream of MFMAs: the score MFMAs of the block in kslot
+// (when do_s), then the P V MFMAs of the block in vslot (when do_pv), with
+// every LDS operand read issued kPpAhead MFMAs ahead of its use (the
+// sched_group_barrier sequence keeps the compiler from pulling them back).
+template <typename T, int D, int DR>
+__device__ __forceinline__ void pp_mphase(const char* __restrict__ kslot, const char* __restrict__ vslot, bool do_s,
+                                          bool do_pv, const PpCtx<T>& x,
+                                          const typename Vec8<T>::type (&qf)[PpCfg<T, D, DR>::NKS],
+                                          const typename Vec8<T>::type (&pk)[2][2], f32x16 (&s)[2],
+                                          f32x16 (&oacc)[PpCfg<T, D, DR>::NDT]) {
+  using C = PpCfg<T, D, DR>;
+  using V8 = typename Vec8<T>::type;
+  constexpr int NS = 2 * C::NKS;  // score MFMAs
+  constexpr int NP = 4 * C::NDT;  // P V MFMAs
+  const char* vs = vslot + C::V_OFF;
+  const int vq = x.lane >> 4, vj = x.lane & 15;
+  auto kread = [&](int i) {
+    const int kstep = i >> 1, t = i & 1;
+    const int r = 32 * t + x.l32;
+    const char* src = kstep < D / 16
+                          ? kslot + (r * C::KU + k_swz(r, 2 * kstep + x.hh)) * 16
+                          : kslot + C::KR_OFF + (r * C::KRU + k_swz(r, 2 * (kstep - D / 16) + x.hh)) * 16;
+    return *reinterpret_cast<const V8*>(src);
+  };
+  // P V MFMA i: output tile dt = i % NDT, key step (t, s2) = i / NDT, so
+  // consecutive MFMAs accumulate into different tiles
+  auto vread = [&](int i) {
+    const int dt = i % C::NDT, t = (i / C::NDT) >> 1, s2 = (i / C::NDT) & 1;
+    const int vu = 4 * dt + 2 * (vq & 1) + ((vj & 3) >> 1);
+    const int r0 = 32 * t + 16 * s2 + 4 * (vq >> 1) + (vj >> 2);
+    const int r1 = r0 + 8;
+    const char* a0 = vs + (r0 * C::VU + v_swz<C::VU>(r0, vu)) * 16 + 8 * (vj & 1);
+    const char* a1 = vs + (r1 * C::VU + v_swz<C::VU>(r1, vu)) * 16 + 8 * (vj & 1);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
+    return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  if (do_s && do_pv) {
+    V8 a[NS + NP];
+#pragma unroll
+    for (int i = 0; i < NS + NP + kPpAhead; ++i) {
+      if (i < NS) a[i] = kread(i);
+      else if (i < NS + NP) a[i] = vread(i - NS);
+      const int j = i - kPpAhead;
+      if (j >= 0 && j < NS) {
+        s[j & 1] = mfma32<T>(a[j], qf[j >> 1], j < 2 ? f32x16{} : s[j & 1]);
+      } else if (j >= NS) {
+        const int q = j - NS, ts = q / C::NDT;
+        oacc[q % C::NDT] = mfma32<T>(a[j], pk[ts >> 1][ts & 1], oacc[q % C::NDT]);
+      }
+    }
+    // keep the reads kPpAhead MFMAs ahead (the scheduler would pull them back)
+    __builtin_amdgcn_sched_group_barrier(0x100, kPpAhead, 0);
+#pragma unroll
+    for (int j = 0; j < NS + NP; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      const int n = j + kPpAhead;
+      if (n < NS)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      else if (n < NS + NP)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  } else if (do_s) {
+    V8 a[NS];
+#pragma unroll
+    for (int i = 0; i < NS + kPpAhead; ++i) {
+      if (i < NS) a[i] = kread(i);
+      const int j = i - kPpAhead;
+      if (j >= 0) s[j & 1] = mfma32<T>(a[j], qf[j >> 1], j < 2 ? f32x16{} : s[j & 1]);
+    }
+  } else if (do_pv) {
+    V8 a[NP];
+#pragma unroll
+    for (int i = 0; i < NP + kPpAhead; ++i) {
+      if (i < NP) a[i] = vread(i);
+      const int q = i - kPpAhead, ts = q / C::NDT;
+      if (q >= 0) oacc[q % C::NDT] = mfma32<T>(a[q], pk[ts >> 1][ts & 1], oacc[q % C::NDT]);
+    }
+  }
+}
+
+// Mask bytes of keys jb + 32t + 8a + 4hh + 0..3 for this lane's row (nonzero = excluded).
+template <typename T>
+__device__ __forceinline__ uint32_t pp_mask_word(const Params& p, const PpCtx<T>& x, int jb, int t, int a) {
+  const int key = jb + 32 * t + 8 * a + 4 * x.hh;
+  if (p.mask_vec4) return (x.row_ok && key < x.skv) ? *reinterpret_cast<const uint32_t*>(x.mrow + key) : 0u;
+  uint32_t v = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    uint32_t byte = 0;
+    if (x.mrow != nullptr && key + b < x.skv && (!p.varlen || key + b < p.m_cols))
+      byte = x.mrow[(int64_t)(key + b) * p.m_sk];
+    else if (p.varlen)
+      byte = 1;  // outside the 2-D mask: excluded
+    v |= (byte ? 0xffu : 0u) << (8 * b);
+  }
+  return v;
+}
+
+// Softmax step of the block at jb (scores in st.sacc) -> st.pk.  Blocks that
+// cross the window edge or the sequence end (or read the mask) first set
+// their excluded scores to -inf.
+template <typename T, int D, int DR>
+__device__ __forceinline__ void pp_softmax(const Params& p, const PpCtx<T>& x, int jb, PpState<T, D, DR>& st) {
+  using C = PpCfg<T, D, DR>;
+  constexpr int BN = C::BN;
+  const bool tail = jb + BN > x.skv;
+  const bool edge = p.band && !(jb >= x.g_last - p.pre && jb + BN - 1 <= x.g_first + p.next);
+  const bool rmask = p.has_mask && (p.mask_everywhere || edge || tail);
+  if (tail || edge || rmask) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const uint32_t mword = rmask ? pp_mask_word(p, x, jb, t, a) : 0u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int j = 4 * a + b;
+          const int key = jb + 32 * t + 8 * a + 4 * x.hh + b;
+          bool k_ok = key < x.skv;
+          if (p.band) k_ok = k_ok && (key - x.row <= p.next) && (x.row - key <= p.pre);
+          k_ok = k_ok && ((mword >> (8 * b)) & 0xffu) == 0;
+          st.sacc[t][j] = k_ok ? st.sacc[t][j] : kNegInf;
+        }
+      }
+    }
+  }
+  const float c = p.scale_log2;
+  float mx;
+  {
+    float m8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = i >> 2, j = 4 * (i & 3);
+      m8[i] = __builtin_fmaxf(__builtin_fmaxf(st.sacc[t][j], st.sacc[t][j + 1]), __builtin_fmaxf(st.sacc[t][j + 2], st.sacc[t][j + 3]));
+    }
+    mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(m8[0], m8[1]), __builtin_fmaxf(m8[2], m8[3])),
+                         __builtin_fmaxf(__builtin_fmaxf(m8[4], m8[5]), __builtin_fmaxf(m8[6], m8[7])));
+  }
+  mx = xhalf_max(mx);
+  const float mxc = mx * c;  // c > 0, so -inf stays -inf
+  st.m_max = __builtin_fmaxf(st.m_max, mxc);
+  if (mxc > st.m_ref + kLazy) {
+    const float alpha = fast_exp2(st.m_ref - mxc);  // 0 when m_ref = -inf
+    st.lsum *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) st.oacc[dt] *= alpha;
+    st.m_ref = mxc;
+  }
+  const float m_use = st.m_ref == kNegInf ? 0.f : st.m_ref;
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float e = fast_exp2(fmaf(st.sacc[t][j], c, -m_use));
+      ls[j & 3] += e;
+      st.pk[t][j >> 3][j & 7] = from_f32<T>(e);
+    }
+  st.lsum += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+}
+
+// One step (phases 2k and 2k + 1).  Reads slot cur (block k) and nxt (block
+// k + 1), fills slot fill with block k + NSLOT - 1.  The three pointers are
+// restrict-qualified, so the compiler knows the operand reads do not depend
+// on the loads in flight.
+template <typename T, int D, int DR>
+__device__ __forceinline__ void pp_step(char* __restrict__ fill, const char* __restrict__ cur,
+                                        const char* __restrict__ nxt, int k, int jb0, bool act_k, bool act_k1,
+                                        int grp, const Params& p, const PpCtx<T>& x, PpState<T, D, DR>& st) {
+  using C = PpCfg<T, D, DR>;
+  constexpr int BN = C::BN;
+  pp_stage<T, D, DR>(fill, jb0 + (k + C::NSLOT - 1) * BN, x);
+  // phase 2k: group 0 = M phase of step k, group 1 = softmax of block k
+  if (grp == 0) {
+    __builtin_amdgcn_s_setprio(1);
+    pp_mphase<T, D, DR>(nxt, cur, act_k1, act_k, x, st.qf, st.pk, st.sacc, st.oacc);
+    __builtin_amdgcn_s_setprio(0);
+  } else {
+    if (k == 0 && act_k) pp_scores<T, D, DR>(cur, x, st.qf, st.sacc);
+    if (act_k) pp_softmax<T, D, DR>(p, x, jb0 + k * BN, st);
+  }
   __builtin_amdgcn_s_barrier();
+  // phase 2k + 1: group 0 = softmax of block k + 1, group 1 = M phase of step k
+  if (grp == 0) {
+    if (act_k1) pp_softmax<T, D, DR>(p, x, jb0 + (k + 1) * BN, st);
+  } else {
+    __builtin_amdgcn_s_setprio(1);
+    pp_mphase<T, D, DR>(nxt, cur, act_k1, act_k, x, st.qf, st.pk, st.sacc, st.oacc);
+    __builtin_amdgcn_s_setprio(0);
+  }
 }
 
 template <typename T, int D, int DR>
@@ -58,17 +341,15 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
   using C = PpCfg<T, D, DR>;
   using V8 = typename Vec8<T>::type;
   constexpr int BN = C::BN;
-  __shared__ __attribute__((aligned(16))) T smem[2 * C::K_ELEMS + 2 * C::V_ELEMS];
-  T* const kbuf0 = smem;
-  T* const vbuf0 = smem + 2 * C::K_ELEMS;
+  constexpr int NSLOT = C::NSLOT;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
 
   const Tile tl = map_tile(p, blockIdx.x);
   if (!tl.valid) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int grp = wave >> 2;          // wave-uniform
-  const int t256 = tid & 255;         // thread index within the group
+  const int grp = wave >> 2;  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const int i0 = tl.qt * kPpBM;
   const int g_first = i0 + 128 * grp;
@@ -76,28 +357,28 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
   const bool row_ok = row < tl.sq;
   const int g = tl.h / p.group;
 
-  // ---- Q^T fragments
-  V8 qf[C::NKS];
+  PpState<T, D, DR> st;
+  // ---- Q^T fragments (B operand): lane holds row `row`, dims 16*ks + 8*hh .. +7
   {
     const int64_t qrow = tl.q_row0 + (row_ok ? row : 0);
     const T* qrowp = static_cast<const T*>(p.q) + tl.b * p.q_sb + tl.h * p.q_sh + qrow * p.q_ss;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qrowp + 16 * ks + 8 * hh) : make_uint4(0, 0, 0, 0);
-      qf[ks] = __builtin_bit_cast(V8, u);
+      st.qf[ks] = __builtin_bit_cast(V8, u);
     }
     if constexpr (DR > 0) {
       const T* qrp = static_cast<const T*>(p.qr) + tl.b * p.qr_sb + tl.h * p.qr_sh + qrow * p.qr_ss;
 #pragma unroll
       for (int ks = 0; ks < DR / 16; ++ks) {
         uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qrp + 16 * ks + 8 * hh) : make_uint4(0, 0, 0, 0);
-        qf[D / 16 + ks] = __builtin_bit_cast(V8, u);
+        st.qf[D / 16 + ks] = __builtin_bit_cast(V8, u);
       }
     }
   }
 
-  // ---- key blocks: the workgroup walks the union of both groups' ranges;
-  // a group skips the blocks outside its own range (still meeting every barrier)
+  // ---- key blocks: the workgroup walks the union of both groups' ranges; a
+  // group skips the blocks outside its own range (still meeting every barrier)
   const int wg_last = min(i0 + kPpBM, tl.sq) - 1;
   int kv_lo, kv_hi;
   key_range(p, i0, wg_last, tl.skv, &kv_lo, &kv_hi);
@@ -112,270 +393,76 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
     return g_rows && k < nblocks && jb <= ghi && jb + BN - 1 >= glo;
   };
 
-  // ---- running state
-  const float c = p.scale_log2;
-  float m_ref = kNegInf, m_max = kNegInf, lsum = 0.f;
+  // ---- running state, log2 domain: t = s * c, c = scale * log2(e)
+  st.m_ref = kNegInf;
+  st.m_max = kNegInf;
+  st.lsum = 0.f;
   if (p.has_sink) {
     const float sk = p.sink[tl.h];
     if (sk > kNegInf) {
-      m_ref = m_max = sk * kLog2e;
-      lsum = hh == 0 ? 1.f : 0.f;
+      st.m_ref = st.m_max = sk * kLog2e;
+      st.lsum = hh == 0 ? 1.f : 0.f;  // 2^(sink - m_ref) = 1, counted once per row
     }
   }
-  f32x16 oacc[C::NDT];
 #pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] = f32x16{};
-  f32x16 sacc[2];
-  V8 pk[2][2];
+  for (int dt = 0; dt < C::NDT; ++dt) st.oacc[dt] = f32x16{};
 
-  // ---- staging: group 0 loads K (+Krope), group 1 loads V
-  const T* kbase = static_cast<const T*>(p.k) + tl.b * p.k_sb + g * p.k_sh + tl.kv_row0 * p.k_ss;
-  const T* vbase = static_cast<const T*>(p.v) + tl.b * p.v_sb + g * p.v_sh + tl.kv_row0 * p.v_ss;
-  const T* krbase =
-      DR ? static_cast<const T*>(p.kr) + tl.b * p.kr_sb + g * p.kr_sh + tl.kv_row0 * p.kr_ss : nullptr;
-  const int64_t krow_b = p.k_ss * (int64_t)sizeof(T), vrow_b = p.v_ss * (int64_t)sizeof(T);
-  const int64_t krrow_b = DR ? p.kr_ss * (int64_t)sizeof(T) : 0;
-  // chunk i of this thread: key (t256 + 256 i) / (D/8), 16-byte column (t256 + 256 i) % (D/8);
-  // offsets are recomputed per use (one multiply-add) rather than held in registers
-  auto k_key = [&](int i, int cols) { return (t256 + 256 * i) / cols; };
-  auto k_col = [&](int i, int cols) { return (t256 + 256 * i) % cols; };
-  const int vkg = t256 & 15, vdg = t256 >> 4;
-  const bool v_active = t256 < C::VBLOCKS;
-  const int voff = (8 * vdg) * C::VS + vt_pos(4 * vkg);
-
-  auto rsrc = [](const void* base, int64_t bytes) {
-    const int n = (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-  };
-  uint4 sreg[C::KCH + C::KRCH > 4 ? C::KCH + C::KRCH : 4];  // this thread's staged chunks
-  auto issue_k = [&](int k) {  // group 0
-    const int jb = jb0 + k * BN;
-    const int64_t rows = min(tl.skv - jb, BN);
-    const auto rk = rsrc(kbase + (int64_t)jb * p.k_ss, rows * krow_b);
-#pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-      const uint32_t off = (uint32_t)(k_key(i, D / 8) * krow_b + k_col(i, D / 8) * 16);
-      sreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-    }
-    if constexpr (DR > 0) {
-      const auto rkr = rsrc(krbase + (int64_t)jb * p.kr_ss, rows * krrow_b);
-#pragma unroll
-      for (int i = 0; i < C::KRCH; ++i) {
-        const uint32_t off = (uint32_t)(k_key(i, DR / 8) * krrow_b + k_col(i, DR / 8) * 16);
-        sreg[C::KCH + i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rkr, off, 0, 0));
-      }
-    }
-  };
-  auto write_k = [&](int buf) {
-    T* st = kbuf0 + buf * C::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < C::KCH; ++i)
-      *reinterpret_cast<uint4*>(st + k_key(i, D / 8) * C::KS + k_col(i, D / 8) * 8) = sreg[i];
-#pragma unroll
-    for (int i = 0; i < C::KRCH; ++i)
-      *reinterpret_cast<uint4*>(st + k_key(i, DR / 8) * C::KS + D + k_col(i, DR / 8) * 8) = sreg[C::KCH + i];
-  };
-  auto issue_v = [&](int k) {  // group 1
-    if (!v_active) return;
-    const int jb = jb0 + k * BN;
-    const int64_t rows = min(tl.skv - jb, BN);
-    const auto rv = rsrc(vbase + (int64_t)jb * p.v_ss, rows * vrow_b);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t off = (uint32_t)((4 * vkg + r) * vrow_b + 16 * vdg);
-      sreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
-    }
-  };
-  auto write_v = [&](int buf) {
-    if (!v_active) return;
-    T* st = vbuf0 + buf * C::V_ELEMS;
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&sreg[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&sreg[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&sreg[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&sreg[3]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      uint32_t lo, hi;
-      if (e & 1) {
-        lo = (w0[w] >> 16) | (w1[w] & 0xffff0000u);
-        hi = (w2[w] >> 16) | (w3[w] & 0xffff0000u);
-      } else {
-        lo = (w0[w] & 0xffffu) | (w1[w] << 16);
-        hi = (w2[w] & 0xffffu) | (w3[w] << 16);
-      }
-      *reinterpret_cast<uint2*>(st + voff + e * C::VS) = make_uint2(lo, hi);
-    }
-  };
-
-  // ---- mask (edge blocks only), fetched one phase ahead of its use
-  const uint8_t* mrow = nullptr;
-  if (p.has_mask) {
+  PpCtx<T> x;
+  x.kbase = static_cast<const T*>(p.k) + tl.b * p.k_sb + g * p.k_sh + tl.kv_row0 * p.k_ss;
+  x.vbase = static_cast<const T*>(p.v) + tl.b * p.v_sb + g * p.v_sh + tl.kv_row0 * p.v_ss;
+  x.krbase = DR ? static_cast<const T*>(p.kr) + tl.b * p.kr_sb + g * p.kr_sh + tl.kv_row0 * p.kr_ss : nullptr;
+  x.krow_b = p.k_ss * (int64_t)sizeof(T);
+  x.vrow_b = p.v_ss * (int64_t)sizeof(T);
+  x.krrow_b = DR ? p.kr_ss * (int64_t)sizeof(T) : 0;
+  x.mrow = nullptr;
+  if (p.has_mask) {  // dense: [b|0, h|0, row, :]; TND: the 2-D mask in local coordinates
     if (p.varlen)
-      mrow = row < p.m_rows ? p.mask + (int64_t)row * p.m_sq : nullptr;
+      x.mrow = row < p.m_rows ? p.mask + (int64_t)row * p.m_sq : nullptr;
     else
-      mrow = p.mask + tl.b * p.m_sb + tl.h * p.m_sh + (int64_t)(row_ok ? row : 0) * p.m_sq;
+      x.mrow = p.mask + tl.b * p.m_sb + tl.h * p.m_sh + (int64_t)(row_ok ? row : 0) * p.m_sq;
   }
-  auto flags = [&](int k, bool* tail, bool* edge, bool* rmask) {
-    const int jb = jb0 + k * BN;
-    *tail = jb + BN > tl.skv;
-    *edge = p.band && !(jb >= g_last - p.pre && jb + BN - 1 <= g_first + p.next);
-    *rmask = p.has_mask && (p.mask_everywhere || *edge || *tail);
-  };
-  // mask bytes of keys jb + 32t + 8a + 4hh + 0..3 for this lane's row (edge blocks only)
-  auto mask_word = [&](int jb, int t, int a) -> uint32_t {
-    const int key = jb + 32 * t + 8 * a + 4 * hh;
-    if (p.mask_vec4) return (row_ok && key < tl.skv) ? *reinterpret_cast<const uint32_t*>(mrow + key) : 0u;
-    uint32_t v = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      uint32_t byte = 0;
-      if (mrow != nullptr && key + b < tl.skv && (!p.varlen || key + b < p.m_cols)) byte = mrow[(int64_t)(key + b) * p.m_sk];
-      else if (p.varlen) byte = 1;  // outside the 2-D mask: excluded
-      v |= (byte ? 0xffu : 0u) << (8 * b);
-    }
-    return v;
-  };
+  x.skv = tl.skv;
+  x.row = row;
+  x.g_first = g_first;
+  x.g_last = g_last;
+  x.lane = lane;
+  x.wave = wave;
+  x.l32 = l32;
+  x.hh = hh;
+  x.row_ok = row_ok;
 
-  // S^T of block k from K buffer `buf`
-  auto scores = [&](int buf) {
-    const T* ks_ = kbuf0 + buf * C::K_ELEMS;
-    sacc[0] = f32x16{};
-    sacc[1] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const V8 a = *reinterpret_cast<const V8*>(ks_ + (32 * t + l32) * C::KS + 16 * ks + 8 * hh);
-        sacc[t] = mfma32<T>(a, qf[ks], sacc[t]);
-      }
-    }
-  };
-  // O^T += V^T P^T with V buffer `buf`
-  auto pv = [&](int buf) {
-    const T* vs_ = vbuf0 + buf * C::V_ELEMS;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const V8 a = *reinterpret_cast<const V8*>(vs_ + (32 * dt + l32) * C::VS + 32 * t + 16 * s2 + 8 * hh);
-          oacc[dt] = mfma32<T>(a, pk[t][s2], oacc[dt]);
-        }
-      }
-    }
-  };
-  // softmax step of block k (scores in sacc) -> pk
-  auto softmax = [&](int k) {
-    const int jb = jb0 + k * BN;
-    bool tail, edge, rmask;
-    flags(k, &tail, &edge, &rmask);
-    if (tail || edge || rmask) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const uint32_t mword = rmask ? mask_word(jb, t, a) : 0u;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int j = 4 * a + b;
-            const int key = jb + 32 * t + 8 * a + 4 * hh + b;
-            bool k_ok = key < tl.skv;
-            if (p.band) k_ok = k_ok && (key - row <= p.next) && (row - key <= p.pre);
-            k_ok = k_ok && ((mword >> (8 * b)) & 0xffu) == 0;
-            sacc[t][j] = k_ok ? sacc[t][j] : kNegInf;
-          }
-        }
-      }
-    }
-    float mx = kNegInf;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = __builtin_fmaxf(mx, sacc[t][j]);
-    mx = xhalf_max(mx);
-    const float mxc = mx * c;
-    m_max = __builtin_fmaxf(m_max, mxc);
-    if (mxc > m_ref + kLazy) {
-      const float alpha = fast_exp2(m_ref - mxc);
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] *= alpha;
-      m_ref = mxc;
-    }
-    const float m_use = m_ref == kNegInf ? 0.f : m_ref;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float e = fast_exp2(fmaf(sacc[t][j], c, -m_use));
-        lsum += e;
-        pk[t][j >> 3][j & 7] = from_f32<T>(e);
-      }
-  };
+  auto slot = [&](int k) { return smem + (k % NSLOT) * C::SLOT; };
 
-  // ---- prologue: K_0, V_0 (and K_1) in LDS; group 0 runs the first softmax
+  // ---- prologue: blocks 0 .. NSLOT - 2 in flight; group 0 runs block 0's
+  // scores and softmax while block 1 lands
   if (nblocks > 0) {
-    if (grp == 0) {
-      issue_k(0);
-      __builtin_amdgcn_s_waitcnt(0x0f70);
-      write_k(0);
-    } else {
-      issue_v(0);
-      __builtin_amdgcn_s_waitcnt(0x0f70);
-      write_v(0);
+#pragma unroll
+    for (int b = 0; b < NSLOT - 1; ++b) pp_stage<T, D, DR>(slot(b), jb0 + b * BN, x);
+    __builtin_amdgcn_s_waitcnt(0x0f70 | ((NSLOT - 2) * C::LPB));  // Q fragments and block 0
+    __builtin_amdgcn_s_barrier();
+    if (grp == 0 && active(0)) {
+      pp_scores<T, D, DR>(slot(0), x, st.qf, st.sacc);
+      pp_softmax<T, D, DR>(p, x, jb0, st);
     }
+    // all prologue blocks: the loop's operand reads then only ever wait on
+    // loads issued inside the loop, whose targets the compiler can tell apart
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __builtin_amdgcn_s_barrier();
   }
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // Q fragments and the first blocks have landed
-  lds_barrier();
-  if (grp == 0) {
-    if (nblocks > 1) {
-      issue_k(1);
-    }
-    if (active(0)) {
-      scores(0);
-      softmax(0);
-    }
-    if (nblocks > 1) {
-      __builtin_amdgcn_s_waitcnt(0x0f70);
-      write_k(1);
-    }
-  }
-  lds_barrier();
 
-  // ---- main loop: phase 2k then phase 2k+1
+  // ---- main loop
   for (int k = 0; k < nblocks; ++k) {
-    // phase 2k: group 0 = M_k, group 1 = softmax of block k (block 0: its scores too)
-    if (grp == 0) {
-      if (k + 2 < nblocks) issue_k(k + 2);
-      if (active(k + 1)) scores((k + 1) & 1);
-      if (active(k)) pv(k & 1);
-    } else {
-      if (k + 1 < nblocks) issue_v(k + 1);
-      if (k == 0 && active(0)) scores(0);
-      if (active(k)) softmax(k);
-    }
-    lds_barrier();
-    // phase 2k+1: group 0 = softmax of block k+1, group 1 = M_k
-    if (grp == 0) {
-      if (k + 2 < nblocks) {
-        __builtin_amdgcn_s_waitcnt(0x0f70);
-        write_k(k & 1);
-      }
-      if (active(k + 1)) softmax(k + 1);
-    } else {
-      if (k + 1 < nblocks) {
-        __builtin_amdgcn_s_waitcnt(0x0f70);
-        write_v((k + 1) & 1);
-      }
-      if (active(k + 1)) scores((k + 1) & 1);
-      if (active(k)) pv(k & 1);
-    }
-    lds_barrier();
+    pp_step<T, D, DR>(slot(k + NSLOT - 1), slot(k), slot(k + 1), k, jb0, active(k), active(k + 1), grp, p, x, st);
+    // block k + 2 has landed (all but the newest NSLOT - 3 blocks)
+    __builtin_amdgcn_s_waitcnt(0x0f70 | ((NSLOT - 3) * C::LPB));
+    __builtin_amdgcn_s_barrier();
   }
 
-  // ---- epilogue
+  float& m_ref = st.m_ref;
+  float& m_max = st.m_max;
+  float& lsum = st.lsum;
+  f32x16 (&oacc)[C::NDT] = st.oacc;
+  // ---- epilogue: O = O / l, statistics at the true max
   const float lref = xhalf_sum(lsum);
   if (!row_ok) return;
   const float inv = lref > 0.f ? 1.f / lref : 0.f;

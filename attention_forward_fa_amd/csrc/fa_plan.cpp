@@ -317,12 +317,17 @@ extern "C" fa_status fa_fwd_get_workspace_size(
                        (dr == 0 || dr == 64) && vec_ok(query->data, q) && vec_ok(key->data, k) &&
                        vec_ok(value->data, v) && vec_ok(attention_out->data, o) &&
                        (!query_rope || (vec_ok(query_rope->data, qr) && vec_ok(key_rope->data, kr))) && stats_vec;
-  // Family: the four-wave matrix-core kernel wherever it applies (it measures
-  // faster than the two-group kernel on every workload here), the generic
-  // kernel for everything else.  FA_FWD_KERNEL=mfma|pp|generic forces a family
-  // (tests and benchmarks); forcing a matrix-core family on a shape it does not
-  // cover is an error.
-  int kind = mfma_ok ? fa::KERNEL_MFMA : fa::KERNEL_GENERIC;
+  // Family: the two-group (ping-pong) matrix-core kernel for long dense
+  // sequences at D = 128 without rope whose window cuts at most the causal
+  // side (it measures faster there: one K / V stream serves 256 query rows);
+  // the four-wave matrix-core kernel wherever else it applies (short or
+  // varlen sequences, rope, sliding windows, D = 64); the generic kernel for
+  // everything else.  FA_FWD_KERNEL=mfma|pp|generic forces a family (tests and
+  // benchmarks); forcing a matrix-core family on a shape it does not cover is
+  // an error.
+  const bool pp_pref = q.d == 128 && dr == 0 && L != L_TND && q.s >= 1024 && k.s >= 1024 &&
+                       (!band || pre >= k.s - 1);
+  int kind = mfma_ok ? (pp_pref ? fa::KERNEL_MFMA_PP : fa::KERNEL_MFMA) : fa::KERNEL_GENERIC;
   if (const char* force = getenv("FA_FWD_KERNEL")) {
     if (!strcmp(force, "generic")) {
       kind = fa::KERNEL_GENERIC;

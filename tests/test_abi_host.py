@@ -87,7 +87,8 @@ def test_dense_headline_plan():
     try:
         assert ws == 0
         d = describe(pl)
-        assert "kernel=mfma " in d and "grid=1536" in d and "block=256" in d and "dtype=bf16" in d, d
+        # long dense sequences, D = 128, no rope: the two-group kernel (256-row tiles)
+        assert "kernel=mfma_pp " in d and "grid=768" in d and "block=512" in d and "dtype=bf16" in d, d
     finally:
         _lib.fa_plan_destroy(pl)
 
@@ -328,6 +329,28 @@ def test_describe_truncates_safely():
     _lib.fa_plan_destroy(pl)
 
 
+@pytest.mark.parametrize("case,family", [
+    ("causal", "mfma_pp"),      # the window cuts only the causal side
+    ("band", "mfma"),           # sliding window: the four-wave kernel
+    ("rope", "mfma"),
+    ("d64", "mfma"),
+])
+def test_family_policy(case, family):
+    S, N = 4096, 4
+    q = desc([1, N, S, 128 if case != "d64" else 64])
+    kw = dict(layout=b"BNSD")
+    if case in ("causal", "band"):
+        kw.update(causal=1, pre=(2**31 - 1) if case == "causal" else 1024, nxt=0)
+    if case == "rope":
+        r = desc([1, N, S, 64])
+        kw.update(qr=r, kr=r)
+    st, ws, pl = plan(q, q, q, q, **kw)
+    assert st == 0, _lib.last_error_message()
+    d = describe(pl)
+    assert f"kernel={family} " in d, d
+    _lib.fa_plan_destroy(pl)
+
+
 def test_small_grid_uses_four_wave_kernel():
     s = [1, 300, 2, 128]
     st, ws, pl = plan(desc(s), desc(s), desc(s), desc(s))
@@ -338,7 +361,7 @@ def test_small_grid_uses_four_wave_kernel():
 
 
 @pytest.mark.parametrize("force,expect", [("mfma", "kernel=mfma grid=1536"), ("pp", "kernel=mfma_pp grid=768"),
-                                          ("generic", "kernel=generic"), ("", "kernel=mfma grid=1536")])
+                                          ("generic", "kernel=generic"), ("", "kernel=mfma_pp grid=768")])
 def test_forced_kernel_family(monkeypatch, force, expect):
     monkeypatch.setenv("FA_FWD_KERNEL", force)
     q, k, v, o = c2()
