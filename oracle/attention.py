@@ -9,7 +9,7 @@ no online rescaling, no exp2, no block skipping.
 What it computes (aclnnFlashAttentionVarLenScoreV5 page, 功能说明 → 计算公式,
 the attention equation and the three sink equations below it):
 
-    s_ij = scale * ( q_i . k_j  +  qrope_i . krope_j )
+    s_ij = scale * ( q_i . k_j  +  qrope_i . krope_j )  +  pse_ij
     masked(i, j)  ->  s_ij = -inf
     m_i  = max( max_j s_ij , sink_h )                  (sink term only if given)
     l_i  = sum_j e^(s_ij - m_i)  +  e^(sink_h - m_i)
@@ -44,6 +44,11 @@ reason in the design notes):
   * GQA: query head h reads key/value head h // (Nq / Nkv) (V5 约束说明 on
     Nq / Nkv); the sink is indexed by the query head.
   * The value head dim Dv may be smaller than Dqk; O has Dv columns.
+  * pse (realShift) is added after the scale, as the attention equation
+    writes it (that order is pseType 1 on the V5 page; the other pseType
+    values are not defined there).  Dense: [B or 1, N, Sq, Skv].  TND: one
+    flat tensor holding, sequence after sequence, an [N, Sq_i, Skv_i] block
+    (V5 约束说明 on realShiftOptional with TND).
 """
 from __future__ import annotations
 
@@ -85,9 +90,12 @@ def head_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: 
                    q_rope: Optional[torch.Tensor] = None, k_rope: Optional[torch.Tensor] = None,
                    mask: Optional[torch.Tensor] = None, causal: bool = False,
                    pre_tokens: Optional[int] = None, next_tokens: Optional[int] = None,
-                   sink: Optional[float] = None, rows: Optional[torch.Tensor] = None
+                   sink: Optional[float] = None, rows: Optional[torch.Tensor] = None,
+                   pse: Optional[torch.Tensor] = None
                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Attention for one (sequence, query head): q [Sq,D], k [Skv,D], v [Skv,Dv].
+
+    ``pse`` is this head's [Sq, Skv] additive position bias (or None).
 
     Returns (O [R, Dv], m [R], l [R]) in float64 for the query rows ``rows``
     (all rows by default).  This is the V5 page's attention equation with its
@@ -111,6 +119,8 @@ def head_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: 
         if qr is not None:
             s = s + qr.index_select(0, r) @ kr.T
         s = scale * s
+        if pse is not None:
+            s = s + pse.index_select(0, r).to(torch.float64)
         keep = keep_matrix(r, skv, mask=mask, causal=causal, pre_tokens=pre_tokens,
                            next_tokens=next_tokens)
         s = s.masked_fill(~keep, NEG_INF)
@@ -189,7 +199,8 @@ def attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, layo
                       next_tokens: Optional[int] = None,
                       cu_seqlens_q: Optional[Sequence[int] | torch.Tensor] = None,
                       cu_seqlens_kv: Optional[Sequence[int] | torch.Tensor] = None,
-                      samples: Optional[Sequence[Tuple[int, int, torch.Tensor]]] = None):
+                      samples: Optional[Sequence[Tuple[int, int, torch.Tensor]]] = None,
+                      pse: Optional[torch.Tensor] = None):
     """Whole-problem oracle in the caller's layout.
 
     Dense layouts return ``(O, m, l)`` with O in the input layout (last dim Dv)
@@ -202,7 +213,7 @@ def attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, layo
     if layout == "TND":
         return _forward_tnd(q, k, v, scale=scale, q_rope=q_rope, k_rope=k_rope, atten_mask=atten_mask,
                             sink=sink, causal=causal, pre_tokens=pre_tokens, next_tokens=next_tokens,
-                            cu_q=cu_seqlens_q, cu_kv=cu_seqlens_kv, samples=samples)
+                            cu_q=cu_seqlens_q, cu_kv=cu_seqlens_kv, samples=samples, pse=pse)
     if layout in ("BSH", "SBH"):
         if heads is None:
             raise ValueError("BSH/SBH need the query head count")
@@ -226,7 +237,8 @@ def attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, layo
                               k_rope=krc[b, g] if krc is not None else None,
                               mask=_mask_slice(atten_mask, b, h), causal=causal,
                               pre_tokens=pre_tokens, next_tokens=next_tokens,
-                              sink=float(sink[h]) if sink is not None else None, rows=rows)
+                              sink=float(sink[h]) if sink is not None else None, rows=rows,
+                              pse=pse[b if pse.shape[0] > 1 else 0, h] if pse is not None else None)
 
     if samples is not None:
         return [one(b, h, torch.as_tensor(rows)) for (b, h, rows) in samples]
@@ -245,7 +257,7 @@ def _as_list(cu) -> list:
 
 
 def _forward_tnd(q, k, v, *, scale, q_rope, k_rope, atten_mask, sink, causal, pre_tokens,
-                 next_tokens, cu_q, cu_kv, samples):
+                 next_tokens, cu_q, cu_kv, samples, pse=None):
     if atten_mask is not None and atten_mask.dim() != 2:
         raise NotImplementedError("with TND only a 2-D [Sq, Skv] mask in sequence-local coordinates")
     cq, ck = _as_list(cu_q), _as_list(cu_kv)
@@ -254,6 +266,18 @@ def _forward_tnd(q, k, v, *, scale, q_rope, k_rope, atten_mask, sink, causal, pr
     T, N, _ = q.shape
     Nkv = k.shape[1]
     group = N // Nkv
+    # start of each sequence's [N, Sq_i, Skv_i] block in the flat pse
+    pse_off = [0]
+    for bi in range(len(cq) - 1):
+        pse_off.append(pse_off[-1] + N * (cq[bi + 1] - cq[bi]) * (ck[bi + 1] - ck[bi]))
+    if pse is not None and pse.numel() != pse_off[-1]:
+        raise ValueError(f"TND pse must hold {pse_off[-1]} values, got {pse.numel()}")
+
+    def pse_block(bi, h):
+        if pse is None:
+            return None
+        lq, lk = cq[bi + 1] - cq[bi], ck[bi + 1] - ck[bi]
+        return pse.reshape(-1)[pse_off[bi]:pse_off[bi + 1]].view(N, lq, lk)[h]
 
     def one(bi, h, rows=None):
         q0, q1, k0, k1 = cq[bi], cq[bi + 1], ck[bi], ck[bi + 1]
@@ -263,7 +287,8 @@ def _forward_tnd(q, k, v, *, scale, q_rope, k_rope, atten_mask, sink, causal, pr
                               k_rope=k_rope[k0:k1, g] if k_rope is not None else None,
                               mask=atten_mask[:q1 - q0, :k1 - k0] if atten_mask is not None else None,
                               causal=causal, pre_tokens=pre_tokens, next_tokens=next_tokens,
-                              sink=float(sink[h]) if sink is not None else None, rows=rows)
+                              sink=float(sink[h]) if sink is not None else None, rows=rows,
+                              pse=pse_block(bi, h))
 
     if samples is not None:
         return [one(bi, h, torch.as_tensor(rows)) for (bi, h, rows) in samples]

@@ -28,8 +28,9 @@ def _kept(i: int, j: int, mask, causal: bool, pre: Optional[int], nxt: Optional[
 
 
 def head(q: Sequence[Sequence[float]], k, v, scale: float, *, qr=None, kr=None, mask=None,
-         causal=False, pre=None, nxt=None, sink: Optional[float] = None):
-    """One (sequence, head): lists q [Sq][D], k [Skv][D], v [Skv][Dv]. Returns (O, m, l) lists."""
+         causal=False, pre=None, nxt=None, sink: Optional[float] = None, pse=None):
+    """One (sequence, head): lists q [Sq][D], k [Skv][D], v [Skv][Dv]; optional pse [Sq][Skv]
+    added to the scaled logits.  Returns (O, m, l) lists."""
     sq, skv = len(q), len(k)
     dv = len(v[0]) if skv else 0
     O: List[List[float]] = []
@@ -43,7 +44,10 @@ def head(q: Sequence[Sequence[float]], k, v, scale: float, *, qr=None, kr=None, 
             terms = [q[i][d] * k[j][d] for d in range(len(q[i]))]
             if qr is not None:
                 terms += [qr[i][d] * kr[j][d] for d in range(len(qr[i]))]
-            logits.append((scale * math.fsum(terms), j))
+            x = scale * math.fsum(terms)
+            if pse is not None:
+                x = x + pse[i][j]
+            logits.append((x, j))
         cands = [x for x, _ in logits]
         has_sink = sink is not None and sink != NEG_INF
         if has_sink:

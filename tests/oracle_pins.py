@@ -449,4 +449,91 @@ def pin_v5_call_example(orc):
     assert ex["actual_seq_q_len"] == [T] and ex["actual_seq_kv_len"] == [T]
 
 
+
+# ---------------------------------------------------------------------------
+# pse (realShift): the additive bias of the attention equation, after the scale
+# ---------------------------------------------------------------------------
+
+def pin_pse_brute_force(orc):
+    """Dense and TND pse against the scalar brute force, with masks, causal, sink and GQA."""
+    g = torch.Generator().manual_seed(21)
+    B, N, Nkv, Sq, Skv, D = 2, 4, 2, 5, 6, 4
+    q, k, v = _rand((B, N, Sq, D), g), _rand((B, Nkv, Skv, D), g), _rand((B, Nkv, Skv, D), g)
+    sink = _rand((N,), g)
+    pses = [_rand((B, N, Sq, Skv), g), _rand((1, N, Sq, Skv), g)]
+    mask = (torch.rand(B, 1, Sq, Skv, generator=g) < 0.3).to(torch.uint8)
+    for pi, causal, use_mask, use_sink in itertools.product(range(2), (False, True), (False, True), (False, True)):
+        pse = pses[pi]
+        got = orc.attention_forward(q, k, v, layout="BNSD", scale=0.45, pse=pse, causal=causal,
+                                    atten_mask=mask if use_mask else None, sink=sink if use_sink else None)
+        for b in range(B):
+            for h in range(N):
+                gh = h // (N // Nkv)
+                o, m, l = brute.head(q[b, h].tolist(), k[b, gh].tolist(), v[b, gh].tolist(), 0.45,
+                                     mask=mask[b, 0].tolist() if use_mask else None, causal=causal,
+                                     sink=float(sink[h]) if use_sink else None,
+                                     pse=pse[b if pse.shape[0] > 1 else 0, h].tolist())
+                tag = f"pse brute dense pse={pi} causal={causal} mask={use_mask} sink={use_sink} b={b} h={h}"
+                _close(got[0][b, h], torch.tensor(o, dtype=F64), tag + " O")
+                _close(got[1][b, h], torch.tensor(m, dtype=F64), tag + " m")
+                _close(got[2][b, h], torch.tensor(l, dtype=F64), tag + " l")
+    # TND: one flat pse, an [N, Sq_i, Skv_i] block per sequence
+    lq, lk = [3, 4, 2], [2, 4, 5]
+    Nt = 2
+    cq = [0] + list(itertools.accumulate(lq))
+    ck = [0] + list(itertools.accumulate(lk))
+    qt, kt, vt = _rand((cq[-1], Nt, D), g), _rand((ck[-1], Nt, D), g), _rand((ck[-1], Nt, D), g)
+    flat = _rand((sum(Nt * a * b_ for a, b_ in zip(lq, lk)),), g)
+    O, M, L = orc.attention_forward(qt, kt, vt, layout="TND", scale=0.45, pse=flat, causal=True,
+                                    cu_seqlens_q=cq, cu_seqlens_kv=ck)
+    off = 0
+    for bi in range(len(lq)):
+        blk = flat[off:off + Nt * lq[bi] * lk[bi]].view(Nt, lq[bi], lk[bi])
+        off += Nt * lq[bi] * lk[bi]
+        for h in range(Nt):
+            o, m, l = brute.head(qt[cq[bi]:cq[bi + 1], h].tolist(), kt[ck[bi]:ck[bi + 1], h].tolist(),
+                                 vt[ck[bi]:ck[bi + 1], h].tolist(), 0.45, causal=True, pse=blk[h].tolist())
+            tag = f"pse brute TND seq={bi} h={h}"
+            _close(O[cq[bi]:cq[bi + 1], h], torch.tensor(o, dtype=F64), tag + " O")
+            _close(M[h, cq[bi]:cq[bi + 1]], torch.tensor(m, dtype=F64), tag + " m")
+            _close(L[h, cq[bi]:cq[bi + 1]], torch.tensor(l, dtype=F64), tag + " l")
+
+
+def pin_pse_sdpa(orc):
+    """SDPA adds a float attn_mask to the scaled scores: exactly the equation's + pse."""
+    g = torch.Generator().manual_seed(22)
+    B, N, S, D = 2, 3, 29, 8
+    q, k, v = _rand((B, N, S, D), g), _rand((B, N, S, D), g), _rand((B, N, S, D), g)
+    pse = 2.0 * _rand((1, N, S, S), g)
+    sc = 0.37
+    O, M, L = orc.attention_forward(q, k, v, layout="BNSD", scale=sc, pse=pse)
+    _close(O, F.scaled_dot_product_attention(q, k, v, attn_mask=pse, scale=sc), "pse sdpa")
+    logits = sc * q @ k.transpose(-1, -2) + pse
+    _close(M + torch.log(L), torch.logsumexp(logits, -1), "pse logsumexp")
+    _close(M, logits.amax(-1), "pse max")
+    O, _, _ = orc.attention_forward(q, k, v, layout="BNSD", scale=sc, pse=pse, causal=True)
+    causal_bias = torch.triu(torch.full((S, S), -math.inf, dtype=F64), 1)
+    _close(O, F.scaled_dot_product_attention(q, k, v, attn_mask=pse + causal_bias, scale=sc), "pse sdpa causal")
+
+
+def pin_pse_row_shift_and_neg_inf(orc):
+    """A per-row constant in pse shifts m and leaves O, l alone; pse = -inf acts as the mask."""
+    g = torch.Generator().manual_seed(23)
+    B, N, S, D = 1, 2, 17, 8
+    q, k, v = _rand((B, N, S, D), g), _rand((B, N, S, D), g), _rand((B, N, S, D), g)
+    pse = _rand((B, N, S, S), g)
+    c = _rand((B, N, S, 1), g) * 3
+    a = orc.attention_forward(q, k, v, layout="BNSD", scale=0.5, pse=pse)
+    b = orc.attention_forward(q, k, v, layout="BNSD", scale=0.5, pse=pse + c)
+    _close(b[0], a[0], "pse row shift O")
+    _close(b[1], a[1] + c[..., 0], "pse row shift m")
+    _close(b[2], a[2], "pse row shift l")
+    mask = (torch.rand(B, N, S, S, generator=g) < 0.4)
+    mask &= ~torch.eye(S, dtype=torch.bool)
+    a = orc.attention_forward(q, k, v, layout="BNSD", scale=0.5, atten_mask=mask.to(torch.uint8))
+    b = orc.attention_forward(q, k, v, layout="BNSD", scale=0.5,
+                              pse=torch.zeros(B, N, S, S, dtype=F64).masked_fill(mask, -math.inf))
+    for x, y, nm in zip(a, b, "Oml"):
+        _close(y, x, f"pse -inf as mask {nm}")
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

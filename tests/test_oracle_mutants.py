@@ -32,6 +32,12 @@ MUTANTS = {
     "empty_row_nan": ("o = torch.where((l > 0).view(-1, 1), num / torch.where(l > 0, l, torch.ones_like(l)).view(-1, 1),", "o = torch.where((l >= 0).view(-1, 1), num / l.view(-1, 1),"),
     "tnd_kv_uses_q_offsets": ("q0, q1, k0, k1 = cq[bi], cq[bi + 1], ck[bi], ck[bi + 1]", "q0, q1, k0, k1 = cq[bi], cq[bi + 1], cq[bi], cq[bi + 1]"),
     "no_neg_inf_guard": ("m_safe = torch.where(finite, m, torch.zeros_like(m))", "m_safe = m"),
+    "pse_before_scale": ("        s = scale * s\n        if pse is not None:\n            s = s + pse.index_select(0, r).to(torch.float64)\n",
+                         "        if pse is not None:\n            s = s + pse.index_select(0, r).to(torch.float64)\n        s = scale * s\n"),
+    "pse_transposed": ("s = s + pse.index_select(0, r).to(torch.float64)", "s = s + pse.T.index_select(0, r).to(torch.float64)"),
+    "pse_batch_broadcast": ("pse=pse[b if pse.shape[0] > 1 else 0, h]", "pse=pse[0, h]"),
+    "pse_tnd_head_major": ("return pse.reshape(-1)[pse_off[bi]:pse_off[bi + 1]].view(N, lq, lk)[h]",
+                           "return pse.reshape(-1)[pse_off[bi]:pse_off[bi + 1]].view(lq, N, lk)[:, h]"),
     "stats_layout_transposed": ("    if layout == \"TND\" and softmax_out_layout == \"same_as_input\":\n        x = x.transpose(0, 1)\n",
                                 "    if layout == \"TND\" and softmax_out_layout == \"\":\n        x = x.transpose(0, 1)\n"),
 }
