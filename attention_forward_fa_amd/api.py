@@ -49,14 +49,15 @@ class ForwardPlan:
                  query_rope=None, key_rope=None, atten_mask=None, sink=None, cu_seqlens_q=None,
                  cu_seqlens_kv=None, causal: bool = False, pre_tokens: int = UNBOUNDED,
                  next_tokens: int = UNBOUNDED, softmax_out_layout: str = "", out=None,
-                 softmax_max=None, softmax_sum=None, inner_precise: int = 0):
+                 softmax_max=None, softmax_sum=None, inner_precise: int = 0, real_shift=None):
         self.device = _check_device(query, key, value, query_rope, key_rope, atten_mask, sink, cu_seqlens_q,
-                                    cu_seqlens_kv, out, softmax_max, softmax_sum)
-        self._keep = (query, key, value, query_rope, key_rope, atten_mask, sink, cu_seqlens_q, cu_seqlens_kv)
+                                    cu_seqlens_kv, out, softmax_max, softmax_sum, real_shift)
+        self._keep = (query, key, value, query_rope, key_rope, atten_mask, sink, cu_seqlens_q, cu_seqlens_kv,
+                      real_shift)
         self.out, self.softmax_max, self.softmax_sum = out, softmax_max, softmax_sum
         self.plan = None
         ws, plan = _lib.fa_fwd_get_workspace_size(
-            query, query_rope, key, key_rope, value, None, atten_mask, sink, cu_seqlens_q, cu_seqlens_kv,
+            query, query_rope, key, key_rope, value, real_shift, atten_mask, sink, cu_seqlens_q, cu_seqlens_kv,
             scale, 1.0, pre_tokens, next_tokens, head_num, layout, inner_precise, 0, causal,
             softmax_out_layout, softmax_max, softmax_sum, out)
         self.plan = plan
@@ -114,11 +115,14 @@ def attention_forward(query: torch.Tensor, key: torch.Tensor, value: torch.Tenso
                       kv_heads: Optional[int] = None, pre_tokens: int = UNBOUNDED, next_tokens: int = UNBOUNDED,
                       sink: Optional[torch.Tensor] = None, query_rope: Optional[torch.Tensor] = None,
                       key_rope: Optional[torch.Tensor] = None, causal: bool = False,
+                      pse: Optional[torch.Tensor] = None,
                       return_softmax_stats: bool = False, return_plan: bool = False):
     """Dense attention forward.
 
     ``layout`` defaults to "BNSD" when ``head_first`` else "BSND"; "BSH" and
     "SBH" need ``heads``.  ``attn_mask``: u8/bool, nonzero = excluded.
+    ``pse``: optional additive bias [B|1, N, Sq, Skv] in the query's dtype,
+    added after the scale (the realShift input).
     ``scale`` defaults to D**-0.5 with D the non-rope head dim.  Returns the
     output, plus (softmax_max, softmax_sum) shaped [B,N,Sq,8] when
     ``return_softmax_stats``.
@@ -139,7 +143,7 @@ def attention_forward(query: torch.Tensor, key: torch.Tensor, value: torch.Tenso
         ssum = torch.empty_like(smax)
     plan = ForwardPlan(query, key, value, layout=layout, scale=scale, head_num=n, query_rope=query_rope,
                        key_rope=key_rope, atten_mask=attn_mask, sink=sink, causal=causal, pre_tokens=pre_tokens,
-                       next_tokens=next_tokens, out=out, softmax_max=smax, softmax_sum=ssum)
+                       next_tokens=next_tokens, out=out, softmax_max=smax, softmax_sum=ssum, real_shift=pse)
     plan.run()
     if return_plan:
         return plan
@@ -157,8 +161,12 @@ def attention_forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
                              q_rope: Optional[torch.Tensor] = None, k_rope: Optional[torch.Tensor] = None,
                              atten_mask: Optional[torch.Tensor] = None, pre_tokens: int = UNBOUNDED,
                              next_tokens: int = UNBOUNDED, softmax_out_layout: str = "",
+                             pse: Optional[torch.Tensor] = None,
                              return_softmax_stats: bool = False, return_plan: bool = False):
     """Varlen (TND) attention forward over sequences packed along T.
+
+    ``pse``: optional additive bias, one flat tensor holding an
+    [N, Sq_i, Skv_i] block per sequence, in sequence order.
 
     ``cu_seqlens_*``: int32 [B+1] on the GPU, leading 0.  ``max_seqlen_*`` and
     ``deterministic`` are accepted and unused (the kernel never needs them;
@@ -184,7 +192,8 @@ def attention_forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
     plan = ForwardPlan(q, k, v, layout="TND", scale=scale, head_num=n, query_rope=q_rope, key_rope=k_rope,
                        atten_mask=atten_mask, sink=sink, cu_seqlens_q=cu_seqlens_q, cu_seqlens_kv=cu_seqlens_k,
                        causal=causal, pre_tokens=pre_tokens, next_tokens=next_tokens,
-                       softmax_out_layout=softmax_out_layout, out=out, softmax_max=smax, softmax_sum=ssum)
+                       softmax_out_layout=softmax_out_layout, out=out, softmax_max=smax, softmax_sum=ssum,
+                       real_shift=pse)
     plan.run()
     if return_plan:
         return plan

@@ -111,4 +111,13 @@ __device__ __forceinline__ void key_range(const Params& p, int i_first, int i_la
   *hi = e;
 }
 
+// Element index of the pse value for (row, key 0) of this tile's (sequence,
+// head): dense [B|1, N, Sq, Skv] by strides; TND from the sequence's block
+// [N, Sq_b, Skv_b] in the flat tensor.  Reads add the key and stay below
+// p.pse_len.
+__device__ __forceinline__ int64_t pse_row_index(const Params& p, const Tile& tl, int row) {
+  if (p.varlen) return p.pse_off[tl.b] + ((int64_t)tl.h * tl.sq + row) * tl.skv;
+  return tl.b * p.ps_sb + tl.h * p.ps_sh + (int64_t)row * p.ps_sq;
+}
+
 }  // namespace fa

@@ -74,6 +74,9 @@ __global__ void __launch_bounds__(kGenericThreads) fa_fwd_generic(const Params p
       mrow = p.mask + tl.b * p.m_sb + tl.h * p.m_sh + (int64_t)(row_ok ? row : 0) * p.m_sq;
   }
 
+  const T* pse = static_cast<const T*>(p.pse);
+  const int64_t prow = p.has_pse && row_ok ? pse_row_index(p, tl, row) : 0;
+
   for (int it = 0; it < nblocks; ++it) {
     const int jb = jb0 + it * BN;
     __syncthreads();
@@ -92,7 +95,8 @@ __global__ void __launch_bounds__(kGenericThreads) fa_fwd_generic(const Params p
     }
     __syncthreads();
 
-    // scores of this lane's row against the BN staged keys, kept in LDS
+    // logits of this lane's row against the BN staged keys in log2 units,
+    // t = s * c + pse * log2(e), kept in LDS
     float* srow = sp_ + lane * (BN + 1);
     uint32_t keep = 0;
     float mx = kNegInf;
@@ -100,6 +104,12 @@ __global__ void __launch_bounds__(kGenericThreads) fa_fwd_generic(const Params p
       float acc = 0.f;
       for (int d = 0; d < DK; ++d) acc = fmaf(sq_[lane * LD + d], sk_[j * LD + d], acc);
       const int key = jb + j;
+      float bias = 0.f;
+      if (p.has_pse && row_ok && key < tl.skv) {
+        const int64_t idx = prow + key;
+        if (idx >= 0 && idx < p.pse_len) bias = to_f32(pse[idx]) * kLog2e;
+      }
+      const float t = fmaf(acc, c, bias);
       bool ok = key < tl.skv;
       if (p.band) ok = ok && (key - row <= p.next) && (row - key <= p.pre);
       if (p.has_mask && ok) {
@@ -109,17 +119,16 @@ __global__ void __launch_bounds__(kGenericThreads) fa_fwd_generic(const Params p
           ok = mrow[(int64_t)key * p.m_sk] == 0;
       }
       keep |= (ok ? 1u : 0u) << j;
-      if (ok) mx = fmaxf(mx, acc);
-      srow[j] = acc;
+      if (ok) mx = fmaxf(mx, t);
+      srow[j] = t;
     }
-    const float mxc = mx == kNegInf ? kNegInf : mx * c;
-    const float m_new = fmaxf(m2, mxc);
+    const float m_new = fmaxf(m2, mx);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     const float alpha = exp2f(m2 - m_use);
     m2 = m_new;
     float ps = 0.f;
     for (int j = 0; j < BN; ++j) {
-      const float e = ((keep >> j) & 1u) ? exp2f(fmaf(srow[j], c, -m_use)) : 0.f;
+      const float e = ((keep >> j) & 1u) ? exp2f(srow[j] - m_use) : 0.f;
       srow[j] = e;
       ps += e;
     }

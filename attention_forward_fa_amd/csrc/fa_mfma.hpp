@@ -109,6 +109,8 @@ struct LoopCtx {
   const T* krbase;
   int64_t krow_b, vrow_b, krrow_b;  // row strides in bytes
   const uint8_t* mrow;              // this lane's mask row (edge blocks)
+  const T* pse;                     // additive bias, or null
+  int64_t prow;                     // element index of this lane's pse row at key 0
   int skv, row, i0, last_row;
   int lane, wave, l32, hh;
   bool row_ok;
@@ -170,7 +172,7 @@ __device__ __forceinline__ BlockKind block_kind(const Params& p, int jb, int skv
   const bool tail = jb + kMfmaBN > skv;
   const bool edge = p.band && !(jb >= last_row - p.pre && jb + kMfmaBN - 1 <= first_row + p.next);
   const bool rm = p.has_mask && (p.mask_everywhere || edge || tail);
-  return {tail || edge || rm, rm};
+  return {tail || edge || rm || p.has_pse, rm};
 }
 
 // Mask bytes of this lane's row for keys jb + 32t + 8a + 4hh + 0..3, word 4t + a
@@ -198,6 +200,38 @@ __device__ __forceinline__ void fetch_mask(uint32_t (&mw)[8], const Params& p, i
   }
 }
 
+// pse values of this lane's row for keys jb + 32t + 8a + 4hh + 0..3, word
+// 4t + a (4 elements of T); keys past the sequence end (or outside the
+// tensor) read as 0, they are excluded anyway.
+template <typename T>
+__device__ __forceinline__ void fetch_pse(uint2 (&pw)[8], const Params& p, int jb, const LoopCtx<T>& x) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int key = jb + 32 * (w >> 2) + 8 * (w & 3) + 4 * x.hh;
+    const int64_t idx = x.prow + key;
+    if (p.pse_vec4) {
+      pw[w] = (x.row_ok && key < x.skv && idx + 3 < p.pse_len) ? *reinterpret_cast<const uint2*>(x.pse + idx)
+                                                                : make_uint2(0, 0);
+    } else {
+      uint16_t e[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const bool ok = x.row_ok && key + b < x.skv && idx + b >= 0 && idx + b < p.pse_len;
+        e[b] = ok ? __builtin_bit_cast(uint16_t, x.pse[idx + b]) : (uint16_t)0;
+      }
+      pw[w] = make_uint2(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16));
+    }
+  }
+}
+
+// Element b of pse word w as f32.
+template <typename T>
+__device__ __forceinline__ float pse_elem(const uint2& w, int b) {
+  const uint32_t half = b < 2 ? w.x : w.y;
+  const uint16_t bits = (uint16_t)(b & 1 ? half >> 16 : half & 0xffffu);
+  return to_f32(__builtin_bit_cast(T, bits));
+}
+
 // One key block: prefetch the next block (and its mask words) into `nxt`,
 // then the scores from `cur`, the softmax step and the output update.  The
 // two stage pointers are restrict-qualified so the compiler knows the LDS
@@ -213,7 +247,7 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
                                           const Params& p, const LoopCtx<T>& x,
                                           const typename Vec8<T>::type (&qf)[MfmaCfg<T, D, DR>::NKS],
                                           f32x16 (&oacc)[MfmaCfg<T, D, DR>::NDT], float& m_ref, float& m_max,
-                                          float& lsum, uint32_t (&mw)[8]) {
+                                          float& lsum, uint32_t (&mw)[8], uint2 (&pw)[8]) {
   using C = MfmaCfg<T, D, DR>;
   using V8 = typename Vec8<T>::type;
   constexpr int BN = C::BN;
@@ -244,7 +278,11 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
           bool k_ok = key < x.skv;
           if (p.band) k_ok = k_ok && (key - row <= p.next) && (row - key <= p.pre);
           if (bk.read_mask) k_ok = k_ok && ((mw[4 * t + (j >> 2)] >> (8 * (j & 3))) & 0xffu) == 0;
-          bias[t][j] = k_ok ? 0.f : kNegInf;
+          float b0 = 0.f;
+          if constexpr (DR == 0) {  // pse and rope do not combine
+            if (p.has_pse) b0 = pse_elem<T>(pw[4 * t + (j >> 2)], j & 3) * p.inv_scale;
+          }
+          bias[t][j] = k_ok ? b0 : kNegInf;
         }
       }
       sacc[0] = mfma32<T>(a0, qf[0], bias[0]);
@@ -258,6 +296,9 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
   if (more) {
     stage_block<T, D, DR>(nxt, jb + BN, x);
     if (block_kind(p, jb + BN, x.skv, x.i0, x.last_row).read_mask) fetch_mask(mw, p, jb + BN, x);
+    if constexpr (DR == 0) {
+      if (p.has_pse) fetch_pse(pw, p, jb + BN, x);
+    }
   }
 
 #pragma unroll
@@ -393,6 +434,8 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
     else
       x.mrow = p.mask + tl.b * p.m_sb + tl.h * p.m_sh + (int64_t)(row_ok ? row : 0) * p.m_sq;
   }
+  x.pse = static_cast<const T*>(p.pse);
+  x.prow = p.has_pse && row_ok ? pse_row_index(p, tl, row) : 0;
   x.skv = tl.skv;
   x.row = row;
   x.i0 = i0;
@@ -404,9 +447,15 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   x.row_ok = row_ok;
 
   uint32_t mw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  uint2 pw[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) pw[w] = make_uint2(0, 0);
   if (nblocks > 0) {
     stage_block<T, D, DR>(smem, jb0, x);
     if (block_kind(p, jb0, x.skv, x.i0, x.last_row).read_mask) fetch_mask(mw, p, jb0, x);
+    if constexpr (DR == 0) {
+      if (p.has_pse) fetch_pse(pw, p, jb0, x);
+    }
   }
   // Wait here once for the Q fragments, the first block and its mask words.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
@@ -415,7 +464,7 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   for (int it = 0; it < nblocks; ++it) {
     const int stg = it & 1;
     key_block<T, D, DR>(smem + stg * C::STAGE_BYTES, smem + (stg ^ 1) * C::STAGE_BYTES, jb0 + it * BN,
-                        it + 1 < nblocks, p, x, qf, oacc, m_ref, m_max, lsum, mw);
+                        it + 1 < nblocks, p, x, qf, oacc, m_ref, m_max, lsum, mw, pw);
     // this thread's loads of the next block landed; then everyone's, before the swap
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();

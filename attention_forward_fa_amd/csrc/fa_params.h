@@ -40,6 +40,8 @@ struct Params {
   const int32_t* cu_q;   // TND only
   const int32_t* cu_kv;  // TND only
   int32_t* tile_prefix;  // TND only: workspace, [nbatch + 1]
+  const void* pse;       // may be null: additive position bias, q's element type
+  int64_t* pse_off;      // TND with pse: workspace, [nbatch + 1] element offset of each sequence's block
 
   // element strides: batch, row (sequence position / token), head
   int64_t q_sb, q_ss, q_sh;
@@ -51,6 +53,8 @@ struct Params {
   int64_t st_sb, st_ss, st_sh;           // statistics (the 8 slots are contiguous)
   int64_t m_sb, m_sh, m_sq, m_sk;        // mask (0 for broadcast dims)
   int32_t m_rows, m_cols;                // TND: extent of the 2-D mask
+  int64_t ps_sb, ps_sh, ps_sq;           // dense pse: batch (0 when broadcast), head, row strides
+  int64_t pse_len;                       // elements in the pse tensor; every read is bounded by it
 
   int32_t nbatch;   // B (dense) or number of sequences (TND)
   int32_t nq, nkv, group;
@@ -65,6 +69,9 @@ struct Params {
   int32_t has_mask, has_sink, varlen;
   int32_t mask_everywhere;  // read the mask in every block (window cuts nothing)
   int32_t mask_vec4;        // dense mask with contiguous, 4-byte aligned rows: read 4 keys at once
+  int32_t has_pse;
+  int32_t pse_vec4;         // dense pse whose 4-key groups are 8-byte aligned: read 4 keys at once
+  float inv_scale;          // 1 / scale: pse enters the raw score accumulator as pse / scale
 
   int32_t tiles_per_head;   // dense: ceil(sq / BM); TND: ceil(tq / BM) + nbatch (upper bound)
   int32_t num_wg;           // grid size

@@ -134,12 +134,12 @@ extern "C" int32_t fa_plan_describe(const fa_plan* plan, char* buf, size_t len) 
   const int n = snprintf(buf, len,
                          "kernel=%s dtype=%s d=%d dr=%d dv=%d bm=%d bn=%d grid=%d block=%d ws=%llu "
                          "varlen=%d band=%d pre=%d next=%d mask=%d mask_everywhere=%d sink=%d "
-                         "nq=%d nkv=%d tiles_per_head=%d reverse=%d",
+                         "nq=%d nkv=%d tiles_per_head=%d reverse=%d pse=%d",
                          plan->kind == fa::KERNEL_MFMA_PP ? "mfma_pp" : (plan->kind == fa::KERNEL_MFMA ? "mfma" : "generic"),
                          dtype_name(plan->dtype), p.d, p.dr,
                          p.dv, plan->bm, plan->bn, p.num_wg, plan->block, (unsigned long long)plan->ws_bytes,
                          p.varlen, p.band, p.pre, p.next, p.has_mask, p.mask_everywhere, p.has_sink, p.nq, p.nkv,
-                         p.tiles_per_head, p.reverse_tiles);
+                         p.tiles_per_head, p.reverse_tiles, p.has_pse);
   return n;
 }
 
@@ -179,6 +179,7 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   if (atten_mask && atten_mask->dtype != FA_DTYPE_U8 && atten_mask->dtype != FA_DTYPE_BOOL)
     return fail(FA_ERR_PARAM_INVALID, "atten_mask dtype %s not u8/bool", dtype_name(atten_mask->dtype));
   if (sink && sink->dtype != FA_DTYPE_F32) return fail(FA_ERR_PARAM_INVALID, "sink dtype must be f32");
+  if (real_shift && real_shift->dtype != dt) return fail(FA_ERR_PARAM_INVALID, "real_shift dtype must equal query's");
   if (softmax_max && softmax_max->dtype != FA_DTYPE_F32) return fail(FA_ERR_PARAM_INVALID, "softmax_max must be f32");
   if (softmax_sum && softmax_sum->dtype != FA_DTYPE_F32) return fail(FA_ERR_PARAM_INVALID, "softmax_sum must be f32");
   const char* sol = softmax_out_layout ? softmax_out_layout : "";
@@ -194,7 +195,7 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   }
 
   // ---- attributes (561103)
-  if (real_shift) return fail(FA_ERR_UNSUPPORTED, "real_shift (pse) is not supported");
+  if (real_shift && query_rope) return fail(FA_ERR_UNSUPPORTED, "real_shift cannot be combined with rope inputs");
   if (keep_prob != 1.0) return fail(FA_ERR_UNSUPPORTED, "keep_prob must be 1 (no dropout)");
   if (sparse_mode != 0) return fail(FA_ERR_UNSUPPORTED, "sparse_mode %lld unsupported (only 0)", (long long)sparse_mode);
   if (inner_precise < 0 || inner_precise > 2) return fail(FA_ERR_UNSUPPORTED, "inner_precise must be 0, 1 or 2");
@@ -245,6 +246,21 @@ extern "C" fa_status fa_fwd_get_workspace_size(
       return fail(FA_ERR_UNSUPPORTED, "cu_seqlens need B+1 >= 2 entries, equal for q and kv");
     if (nbatch > 20000) return fail(FA_ERR_UNSUPPORTED, "more than 20000 sequences");
     if (!cu_seqlens_q->data || !cu_seqlens_kv->data) return fail(FA_ERR_PARAM_NULLPTR, "cu_seqlens data is NULL");
+  }
+
+  if (real_shift) {
+    const fa_tensor* r = real_shift;
+    if (!r->data) return fail(FA_ERR_PARAM_NULLPTR, "real_shift data is NULL");
+    if (L == L_TND) {
+      if (r->ndim != 1) return fail(FA_ERR_UNSUPPORTED, "TND real_shift must be 1-D: [N*Sq_i*Skv_i over sequences]");
+      if (r->stride[0] != 1) return fail(FA_ERR_PARAM_INVALID, "real_shift must be contiguous");
+    } else {
+      if (r->ndim != 4 || !(r->shape[0] == q.b || r->shape[0] == 1) || r->shape[1] != q.n || r->shape[3] != k.s)
+        return fail(FA_ERR_UNSUPPORTED, "real_shift shape must be [B|1, N, Sq, Skv]");
+      if (r->shape[2] != q.s)
+        return fail(FA_ERR_UNSUPPORTED, "real_shift must have Sq rows (the compressed last-1024-rows form is not supported)");
+      if (r->stride[3] != 1) return fail(FA_ERR_PARAM_INVALID, "real_shift last dimension must be contiguous");
+    }
   }
 
   if (atten_mask) {
@@ -326,7 +342,7 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   // benchmarks); forcing a matrix-core family on a shape it does not cover is
   // an error.
   const bool pp_pref = q.d == 128 && dr == 0 && L != L_TND && q.s >= 1024 && k.s >= 1024 &&
-                       (!band || pre >= k.s - 1);
+                       (!band || pre >= k.s - 1) && !real_shift;
   int kind = mfma_ok ? (pp_pref ? fa::KERNEL_MFMA_PP : fa::KERNEL_MFMA) : fa::KERNEL_GENERIC;
   if (const char* force = getenv("FA_FWD_KERNEL")) {
     if (!strcmp(force, "generic")) {
@@ -335,6 +351,10 @@ extern "C" fa_status fa_fwd_get_workspace_size(
       if (!mfma_ok) {
         delete pl;
         return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL=%s: shape, dtype or alignment not covered", force);
+      }
+      if (!strcmp(force, "pp") && real_shift) {
+        delete pl;
+        return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL=pp: the two-group kernel takes no real_shift");
       }
       kind = !strcmp(force, "pp") ? fa::KERNEL_MFMA_PP : fa::KERNEL_MFMA;
     } else if (force[0] != '\0') {
@@ -382,6 +402,23 @@ extern "C" fa_status fa_fwd_get_workspace_size(
       p.m_cols = (int32_t)(m->shape[1] < (1 << 24) ? m->shape[1] : (1 << 24));
     }
   }
+  p.pse = real_shift ? real_shift->data : nullptr;
+  p.pse_off = nullptr;  // set from the workspace in phase 2
+  p.has_pse = real_shift != nullptr;
+  p.ps_sb = p.ps_sh = p.ps_sq = 0;
+  p.pse_len = 0;
+  if (real_shift) {
+    const fa_tensor* r = real_shift;
+    p.pse_len = 1;
+    for (int i = 0; i < r->ndim; ++i) p.pse_len *= r->shape[i];
+    if (r->ndim == 4) {
+      p.ps_sb = r->shape[0] > 1 ? r->stride[0] : 0;
+      p.ps_sh = r->stride[1];
+      p.ps_sq = r->stride[2];
+      // every element the strides can reach bounds the reads
+      p.pse_len = (r->shape[0] - 1) * p.ps_sb + (r->shape[1] - 1) * p.ps_sh + (r->shape[2] - 1) * p.ps_sq + r->shape[3];
+    }
+  }
   p.nbatch = (int32_t)nbatch;
   p.nq = (int32_t)q.n;
   p.nkv = (int32_t)k.n;
@@ -400,6 +437,9 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   // resolution (every weight is then exactly 1, as with scale 0).
   p.scale_log2 = (float)(scale_value * 1.4426950408889634);
   if (!(p.scale_log2 > 1e-30f)) p.scale_log2 = 1e-30f;
+  // pse enters the raw (unscaled) score accumulator as pse * inv_scale, so
+  // that times scale_log2 it becomes pse * log2(e)
+  p.inv_scale = (float)(1.4426950408889634 / (double)p.scale_log2);
   p.band = band;
   p.pre = (int32_t)pre;
   p.next = (int32_t)nxt;
@@ -413,13 +453,17 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   p.mask_vec4 = p.has_mask && !p.varlen && p.m_sk == 1 && (reinterpret_cast<uintptr_t>(p.mask) & 3u) == 0 &&
                 p.m_sq % 4 == 0 && p.m_sb % 4 == 0 && p.m_sh % 4 == 0;
   p.reverse_tiles = band && nxt < max_keys - 1;
+  p.pse_vec4 = p.has_pse && !p.varlen && (reinterpret_cast<uintptr_t>(p.pse) & 7u) == 0 && p.ps_sq % 4 == 0 &&
+               p.ps_sb % 4 == 0 && p.ps_sh % 4 == 0;
 
   const int64_t bm = pl->bm;
   int64_t tiles, wg;
   if (p.varlen) {
     tiles = cdiv(q.s, bm) + nbatch;
     wg = q.s > 0 ? tiles * q.n : 0;
+    // tile prefix (int32), then with pse each sequence's offset into it (int64, 8-aligned)
     pl->ws_bytes = (uint64_t)(nbatch + 1) * sizeof(int32_t);
+    if (p.has_pse) pl->ws_bytes = (pl->ws_bytes + 7) / 8 * 8 + (uint64_t)(nbatch + 1) * sizeof(int64_t);
   } else {
     tiles = cdiv(q.s, bm);
     wg = tiles * q.b * q.n;

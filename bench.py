@@ -51,7 +51,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2_dense_bsnd",
-                    choices=["c2_dense_bsnd", "c3_causal", "c3_band", "c4_varlen_causal", "c5_varlen_sink_rope"])
+                    choices=["c2_dense_bsnd", "c3_causal", "c3_band", "c4_varlen_causal", "c5_varlen_sink_rope",
+                             "c6_dense_pse"])
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -115,7 +116,7 @@ def flops_per_pair(case) -> int:
 def algorithmic_bytes(case) -> int:
     """Inputs read once, output and statistics written once."""
     tot = 0
-    for t in (case.q, case.k, case.v, case.q_rope, case.k_rope, case.atten_mask, case.sink):
+    for t in (case.q, case.k, case.v, case.q_rope, case.k_rope, case.atten_mask, case.sink, case.pse):
         if t is not None:
             tot += t.numel() * t.element_size()
     tot += case.q.numel() // case.q.shape[-1] * case.v.shape[-1] * case.q.element_size()  # O
@@ -171,7 +172,7 @@ def cpu_baseline(case, budget_s: float):
                               k_rope=case.k_rope, atten_mask=case.atten_mask, sink=case.sink, causal=case.causal,
                               pre_tokens=case.pre_tokens, next_tokens=case.next_tokens,
                               cu_seqlens_q=case.cu_seqlens_q, cu_seqlens_kv=case.cu_seqlens_kv,
-                              samples=[(b, h, rows)])
+                              samples=[(b, h, rows)], pse=case.pse)
         units += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -236,7 +237,7 @@ def main():
                                sink=g["sink"], cu_seqlens_q=g["cu_seqlens_q"], cu_seqlens_kv=g["cu_seqlens_kv"],
                                causal=case.causal, pre_tokens=case.pre_tokens, next_tokens=case.next_tokens,
                                softmax_out_layout=case.softmax_out_layout, out=out, softmax_max=smax,
-                               softmax_sum=ssum)
+                               softmax_sum=ssum, real_shift=g["pse"])
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -257,7 +258,7 @@ def main():
     def step(ev_pair=None):
         # phase 1 + phase 2; the workspace is allocated once, outside the timed region
         wsz, h = _lib.fa_fwd_get_workspace_size(
-            g["q"], g["q_rope"], g["k"], g["k_rope"], g["v"], None, g["atten_mask"], g["sink"], g["cu_seqlens_q"],
+            g["q"], g["q_rope"], g["k"], g["k_rope"], g["v"], g["pse"], g["atten_mask"], g["sink"], g["cu_seqlens_q"],
             g["cu_seqlens_kv"], case.scale, 1.0, case.pre_tokens, case.next_tokens, nheads, case.layout, 0, 0,
             case.causal, case.softmax_out_layout, smax, ssum, out)
         if ev_pair is not None:
@@ -318,7 +319,7 @@ def main():
                    "causal": case.causal, "mask": case.atten_mask is not None,
                    "pre_tokens": case.pre_tokens, "next_tokens": case.next_tokens,
                    "rope_dim": case.q_rope.shape[-1] if case.q_rope is not None else 0,
-                   "sink": case.sink is not None, "scale": case.scale},
+                   "sink": case.sink is not None, "pse": case.pse is not None, "scale": case.scale},
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": roof,
         "kernel": {"name": "fa_fwd_" + desc.split()[0].split("=")[1], "plan": desc,

@@ -56,12 +56,13 @@ class Case:
     cu_seqlens_q: Optional[torch.Tensor] = None
     cu_seqlens_kv: Optional[torch.Tensor] = None
     softmax_out_layout: str = ""
+    pse: Optional[torch.Tensor] = None
 
     def tensors(self) -> Dict[str, Optional[torch.Tensor]]:
         return {
             "q": self.q, "k": self.k, "v": self.v, "q_rope": self.q_rope,
             "k_rope": self.k_rope, "atten_mask": self.atten_mask, "sink": self.sink,
-            "cu_seqlens_q": self.cu_seqlens_q, "cu_seqlens_kv": self.cu_seqlens_kv,
+            "cu_seqlens_q": self.cu_seqlens_q, "cu_seqlens_kv": self.cu_seqlens_kv, "pse": self.pse,
         }
 
 
@@ -120,8 +121,11 @@ def dense_case(name: str, layout: str, b: int, nq: int, sq: int, d: int, dtype: 
                skv: Optional[int] = None, nkv: Optional[int] = None, dv: Optional[int] = None,
                drope: int = 0, sink: bool = False, causal: bool = False, mask: bool = False,
                pre_tokens: int = UNBOUNDED, next_tokens: int = UNBOUNDED,
-               scale: Optional[float] = None) -> Case:
-    """A dense (BNSD / BSND / BSH / SBH) problem with seeded iid N(0,1) tensors."""
+               scale: Optional[float] = None, pse: Optional[str] = None) -> Case:
+    """A dense (BNSD / BSND / BSH / SBH) problem with seeded iid N(0,1) tensors.
+
+    ``pse``: None, "full" ([B, N, Sq, Skv]) or "bcast" ([1, N, Sq, Skv]); drawn
+    after every other tensor, in the working dtype."""
     skv = sq if skv is None else skv
     nkv = nq if nkv is None else nkv
     dv = d if dv is None else dv
@@ -134,17 +138,20 @@ def dense_case(name: str, layout: str, b: int, nq: int, sq: int, d: int, dtype: 
     kr = normal(_shape(layout, b, nkv, skv, drope), g, rope_dt) if drope else None
     sk = normal((nq,), g, torch.float32) if sink else None
     am = lower_triangular_mask(sq, skv) if mask else None
+    ps = normal((b if pse == "full" else 1, nq, sq, skv), g, dtype) if pse else None
     return Case(name=name, layout=layout, q=q, k=k, v=v, q_rope=qr, k_rope=kr,
                 scale=(d ** -0.5) if scale is None else scale, atten_mask=am, sink=sk,
-                causal=causal, pre_tokens=pre_tokens, next_tokens=next_tokens)
+                causal=causal, pre_tokens=pre_tokens, next_tokens=next_tokens, pse=ps)
 
 
 def varlen_case(name: str, lengths_q: Sequence[int], nq: int, d: int, dtype: str, seed: int, *,
                 lengths_kv: Optional[Sequence[int]] = None, nkv: Optional[int] = None,
                 dv: Optional[int] = None, drope: int = 0, sink: bool = False, causal: bool = False,
                 pre_tokens: int = UNBOUNDED, next_tokens: int = UNBOUNDED,
-                scale: Optional[float] = None, softmax_out_layout: str = "") -> Case:
-    """A TND problem: sequences packed along T, described by int32 cumulative lengths."""
+                scale: Optional[float] = None, softmax_out_layout: str = "", pse: bool = False) -> Case:
+    """A TND problem: sequences packed along T, described by int32 cumulative lengths.
+
+    ``pse``: draw a flat bias holding an [N, Sq_i, Skv_i] block per sequence."""
     lengths_kv = list(lengths_q) if lengths_kv is None else list(lengths_kv)
     nkv = nq if nkv is None else nkv
     dv = d if dv is None else dv
@@ -157,11 +164,13 @@ def varlen_case(name: str, lengths_q: Sequence[int], nq: int, d: int, dtype: str
     qr = normal((tq, nq, drope), g, rope_dt) if drope else None
     kr = normal((tkv, nkv, drope), g, rope_dt) if drope else None
     sk = normal((nq,), g, torch.float32) if sink else None
+    npse = sum(nq * a * b for a, b in zip(lengths_q, lengths_kv))
+    ps = normal((npse,), g, dtype) if pse else None
     return Case(name=name, layout="TND", q=q, k=k, v=v, q_rope=qr, k_rope=kr,
                 scale=(d ** -0.5) if scale is None else scale, sink=sk, causal=causal,
                 pre_tokens=pre_tokens, next_tokens=next_tokens,
                 cu_seqlens_q=cu_from_lengths(lengths_q), cu_seqlens_kv=cu_from_lengths(lengths_kv),
-                softmax_out_layout=softmax_out_layout)
+                softmax_out_layout=softmax_out_layout, pse=ps)
 
 
 # ---------------------------------------------------------------------------
@@ -171,7 +180,7 @@ def varlen_case(name: str, lengths_q: Sequence[int], nq: int, d: int, dtype: str
 # ---------------------------------------------------------------------------
 
 WORKLOADS = ("c1_fp32_bnsd", "c2_dense_bsnd", "c3_causal", "c3_band", "c4_varlen_causal",
-             "c5_varlen_sink_rope")
+             "c5_varlen_sink_rope", "c6_dense_pse")
 
 
 def c4_lengths(seed: int = 4, n: int = 16, total: int = 8192) -> List[int]:
@@ -200,4 +209,8 @@ def workload(name: str, dtype: str = "bf16", small: bool = False) -> Case:
                                sink=True, causal=True, scale=128 ** -0.5)
         return varlen_case(name, [2048] * 8, 64, 128, "bf16", seed=5, drope=64, sink=True,
                            causal=True, scale=128 ** -0.5)
+    if name == "c6_dense_pse":
+        # the additive bias term: a full [B, N, S, S] pse makes the pass HBM-bound
+        s = 4096 if not small else 300
+        return dense_case(name, "BNSD", 1, 8 if not small else 2, s, 128, "bf16", seed=6, pse="full")
     raise KeyError(name)

@@ -52,12 +52,13 @@ def run_gpu(case: synth.Case, *, stats: bool = True, layout_heads: Optional[int]
             g["q"], g["k"], g["v"], g["cu_seqlens_q"], g["cu_seqlens_kv"], softmax_scale=case.scale,
             causal=case.causal, sink=g["sink"], q_rope=g["q_rope"], k_rope=g["k_rope"], atten_mask=g["atten_mask"],
             pre_tokens=case.pre_tokens, next_tokens=case.next_tokens, softmax_out_layout=case.softmax_out_layout,
-            return_softmax_stats=stats)
+            pse=g["pse"], return_softmax_stats=stats)
     else:
         res = api.attention_forward(
             g["q"], g["k"], g["v"], attn_mask=g["atten_mask"], scale=case.scale, layout=case.layout,
             heads=layout_heads, pre_tokens=case.pre_tokens, next_tokens=case.next_tokens, sink=g["sink"],
-            query_rope=g["q_rope"], key_rope=g["k_rope"], causal=case.causal, return_softmax_stats=stats)
+            query_rope=g["q_rope"], key_rope=g["k_rope"], causal=case.causal, pse=g["pse"],
+            return_softmax_stats=stats)
     torch.cuda.synchronize()
     if stats:
         return tuple(x.cpu() for x in res)
@@ -70,7 +71,7 @@ def run_oracle(case: synth.Case, heads: Optional[int] = None):
         case.q, case.k, case.v, layout=case.layout, scale=case.scale, heads=heads, q_rope=case.q_rope,
         k_rope=case.k_rope, atten_mask=case.atten_mask, sink=case.sink, causal=case.causal,
         pre_tokens=case.pre_tokens, next_tokens=case.next_tokens, cu_seqlens_q=case.cu_seqlens_q,
-        cu_seqlens_kv=case.cu_seqlens_kv)
+        cu_seqlens_kv=case.cu_seqlens_kv, pse=case.pse)
     if case.layout == "TND" and case.softmax_out_layout == "same_as_input":
         M, L = M.transpose(0, 1), L.transpose(0, 1)
     return O, M, L
@@ -144,7 +145,7 @@ def compare_sampled(case: synth.Case, samples, o, smax, ssum):
         case.q, case.k, case.v, layout=case.layout, scale=case.scale, q_rope=case.q_rope, k_rope=case.k_rope,
         atten_mask=case.atten_mask, sink=case.sink, causal=case.causal, pre_tokens=case.pre_tokens,
         next_tokens=case.next_tokens, cu_seqlens_q=case.cu_seqlens_q, cu_seqlens_kv=case.cu_seqlens_kv,
-        samples=samples)
+        samples=samples, pse=case.pse)
     dt = case.q.dtype
     errs = {"O": 0.0, "m": 0.0, "logl": 0.0}
     for (b, h, rows), (Or, Mr, Lr) in zip(samples, res):

@@ -205,7 +205,7 @@ def test_invalid_formats(case):
     assert pl is None
 
 
-@pytest.mark.parametrize("case", ["keep_prob", "sparse", "pse", "inner", "scale_neg", "scale_nan", "heads",
+@pytest.mark.parametrize("case", ["keep_prob", "sparse", "pse_compressed", "inner", "scale_neg", "scale_nan", "heads",
                                   "gqa_ratio", "d_mismatch", "dv_gt_d", "batch", "kv_rows", "out_shape",
                                   "mask_shape", "sink_shape", "stats_shape", "window_empty", "cu_dense",
                                   "tnd_mask_4d", "big_d", "cu_len"])
@@ -216,8 +216,8 @@ def test_unsupported(case):
         kw["keep"] = 0.9
     elif case == "sparse":
         kw["sparse"] = 2
-    elif case == "pse":
-        kw["pse"] = desc([2, 24, 4096, 4096])
+    elif case == "pse_compressed":  # the last-1024-rows alibi form is not supported
+        kw["pse"] = desc([2, 24, 1024, 4096])
     elif case == "inner":
         kw["inner"] = 3
     elif case == "scale_neg":
@@ -381,4 +381,56 @@ def test_forced_kernel_errors(monkeypatch):
     monkeypatch.setenv("FA_FWD_KERNEL", "fastest")
     q, k, v, o = c2()
     st, _, pl = plan(q, k, v, o)
+    assert st == 561103 and pl is None
+
+
+# ---------------------------------------------------------------------------
+# pse (real_shift)
+# ---------------------------------------------------------------------------
+
+def test_pse_plan_and_validation():
+    B, N, S, D = 2, 4, 512, 128
+    q = desc([B, N, S, D])
+    ok = desc([B, N, S, S])
+    st, ws, pl = plan(q, q, q, q, pse=ok, layout=b"BNSD")
+    assert st == 0, _lib.last_error_message()
+    d = describe(pl)
+    assert "pse=1" in d and "kernel=mfma " in d, d
+    _lib.fa_plan_destroy(pl)
+    st, _, pl = plan(q, q, q, q, pse=desc([1, N, S, S]), layout=b"BNSD")  # broadcast over batch
+    assert st == 0, _lib.last_error_message()
+    _lib.fa_plan_destroy(pl)
+    # long dense D=128 would pick the two-group kernel, which takes no pse
+    q4 = desc([1, N, 4096, D])
+    st, _, pl = plan(q4, q4, q4, q4, pse=desc([1, N, 4096, 4096]), layout=b"BNSD")
+    assert st == 0 and "kernel=mfma " in describe(pl), describe(pl)
+    _lib.fa_plan_destroy(pl)
+    bad = [
+        (dict(pse=desc([B, N, S, S], F16)), 161002),            # dtype differs from query's
+        (dict(pse=desc([B, N, S])), 561103),                    # rank
+        (dict(pse=desc([B, 1, S, S])), 561103),                 # heads must be N
+        (dict(pse=desc([B, N, 1024 if S > 1024 else S - 1, S])), 561103),  # not Sq rows
+        (dict(pse=ok, qr=desc([B, N, S, 64]), kr=desc([B, N, S, 64])), 561103),  # with rope
+    ]
+    for kw, code in bad:
+        st, _, pl = plan(q, q, q, q, layout=b"BNSD", **kw)
+        assert st == code and pl is None, (kw, st, _lib.last_error_message())
+
+
+def test_pse_forced_pp_rejected(monkeypatch):
+    monkeypatch.setenv("FA_FWD_KERNEL", "pp")
+    q = desc([1, 2, 256, 128])
+    st, _, pl = plan(q, q, q, q, pse=desc([1, 2, 256, 256]), layout=b"BNSD")
+    assert st == 561103 and pl is None and "FA_FWD_KERNEL" in _lib.last_error_message()
+
+
+def test_pse_tnd_workspace():
+    T, N = 1000, 2
+    q = desc([T, N, 128])
+    cu = desc([6], I32)
+    st, ws, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND", pse=desc([12345]))
+    assert st == 0, _lib.last_error_message()
+    assert ws == 24 + 8 * 6  # tile prefix (6 int32, padded to 8 bytes) + 6 int64 offsets
+    _lib.fa_plan_destroy(pl)
+    st, _, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND", pse=desc([10, 10]))
     assert st == 561103 and pl is None

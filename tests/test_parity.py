@@ -73,7 +73,27 @@ SMALL = {
     "len_63_65": lambda: synth.varlen_case("x", [63, 64, 65, 127, 128, 129], 2, 128, "bf16", 55),
     "sink_neg_inf": lambda: _sink_neg_inf_case(56),
     "large_logits": lambda: synth.dense_case("x", "BNSD", 1, 2, 200, 128, "bf16", 57, scale=1.0),
+    # additive position bias (pse / realShift)
+    "c6_small_pse": lambda: synth.workload("c6_dense_pse", small=True),
+    "pse_full_bsnd_ragged": lambda: synth.dense_case("x", "BSND", 2, 3, 201, 128, "bf16", 70, pse="full"),
+    "pse_bcast_causal_fp16": lambda: synth.dense_case("x", "BNSD", 2, 2, 170, 128, "fp16", 71, pse="bcast",
+                                                      causal=True),
+    "pse_d64_sink_band": lambda: _pse_band_mask_case(72),
+    "pse_gqa": lambda: synth.dense_case("x", "BNSD", 1, 4, 140, 128, "bf16", 73, nkv=2, pse="full"),
+    "pse_fp32": lambda: synth.dense_case("x", "BNSD", 1, 2, 75, 64, "fp32", 74, pse="full", causal=True),
+    "pse_tnd": lambda: synth.varlen_case("x", [100, 0, 37, 140], 2, 128, "bf16", 75, causal=True, pse=True),
+    "pse_tnd_sink_fp16": lambda: synth.varlen_case("x", [64, 65, 3], 3, 64, "fp16", 76, sink=True, pse=True),
+    "pse_unaligned_rows": lambda: synth.dense_case("x", "BNSD", 1, 2, 130, 128, "bf16", 77, skv=131, pse="full"),
 }
+
+
+def _pse_band_mask_case(seed):
+    c = synth.dense_case("x", "BNSD", 1, 2, 230, 64, "bf16", seed, sink=True, pse="full")
+    i = torch.arange(230).view(-1, 1)
+    j = torch.arange(230).view(1, -1)
+    c.atten_mask = (((j - i) > 4) | ((i - j) > 40)).to(torch.uint8)
+    c.pre_tokens, c.next_tokens = 40, 4
+    return c
 
 
 def _band_mask_case(seed, pre, nxt, dtype="bf16", d=128):
@@ -246,7 +266,7 @@ def test_v5_call_example_on_gpu():
 # full-size workloads, sampled rows
 # ---------------------------------------------------------------------------
 
-FULL = ["c2_bf16", "c2_fp16", "c3_causal", "c3_band", "c4_varlen_causal", "c5_varlen_sink_rope"]
+FULL = ["c2_bf16", "c2_fp16", "c3_causal", "c3_band", "c4_varlen_causal", "c5_varlen_sink_rope", "c6_dense_pse"]
 
 
 def _full_case(name):
