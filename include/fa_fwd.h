@@ -4,7 +4,7 @@
  * Computes, per (batch or sequence, query head), the attention forward of the
  * aclnnFlashAttentionVarLenScoreV5 page (功能说明 -> 计算公式):
  *
- *     Attention = Softmax( Mask( scale * (Q K^T + Qrope Krope^T) ), atten_mask ) * V
+ *     Attention = Softmax( Mask( scale * (Q K^T + Qrope Krope^T) + pse ), atten_mask ) * V
  *
  * with the optional per-head sink logit of the same section (m = max(sink,
  * max S); the denominator gains e^(sink - m)), and writes the per-row
@@ -92,7 +92,17 @@ typedef int32_t fa_status;
  *   query_rope, key_rope  optional, both or neither; F16 or BF16 equal to q's
  *                       dtype, same layout and sizes as query / key with their
  *                       own last dim Dr.  Adds Qrope Krope^T to the scores.
- *   real_shift          pse: must be NULL (the additive bias is not built).
+ *   real_shift          optional pse, q's dtype: the additive position bias
+ *                       of the attention equation, added after the scale
+ *                       (pseType 1; the V5 parameter table, row
+ *                       realShiftOptional).  Dense: [B|1, N, Sq, Skv], last
+ *                       dim contiguous, any other strides.  TND: 1-D, one
+ *                       [N, Sq_i, Skv_i] block per sequence in sequence
+ *                       order (reads beyond shape[0] return 0: the caller
+ *                       keeps the length equal to sum_i N * Sq_i * Skv_i).
+ *                       Not with query_rope / key_rope; the compressed
+ *                       last-1024-rows form is not supported.  With a scale
+ *                       of 0 the bias must stay below 2e8 in magnitude.
  *   atten_mask          optional U8/BOOL, nonzero = position EXCLUDED.
  *                       Dense: [B,N,Sq,Skv], [B,1,Sq,Skv], [1,1,Sq,Skv] or
  *                       [Sq,Skv] (any strides).  TND: a 2-D [S1,S2] matrix
@@ -132,14 +142,18 @@ typedef int32_t fa_status;
  *   attention_out       output, q's dtype, q's layout with last dim Dv.  Rows
  *                       with no kept key are 0.  Rounded to nearest even.
  *   workspace_size      host out: bytes of device workspace phase 2 needs
- *                       (0 for dense layouts).
+ *                       (0 for dense layouts; for TND 4 (B+1) bytes, rounded
+ *                       up to 8 and followed by 8 (B+1) more with real_shift,
+ *                       in which case the workspace must be 8-byte aligned).
  *   plan                host out: a new plan, to be released with
  *                       fa_plan_destroy().  It records the tensors' device
  *                       addresses; it may be executed any number of times.
  *
- * Kernel choice: the matrix-core kernel when q is F16/BF16, D is 64 or 128,
- * Dr is 0 or 64, Dv == D and every row start is 16-byte aligned; otherwise
- * the generic one (fp32 dot products on the vector units).  The environment
+ * Kernel choice: a matrix-core kernel when q is F16/BF16, D is 64 or 128,
+ * Dr is 0 or 64, Dv == D and every row start is 16-byte aligned (the
+ * two-group one for dense Sq, Skv >= 1024 at D = 128 without rope or pse
+ * whose window cuts at most the causal side, else the four-wave one);
+ * otherwise the generic one (fp32 dot products on the vector units).  The environment
  * variable FA_FWD_KERNEL = "mfma" | "pp" | "generic", read here, forces a
  * family for testing; forcing one the arguments do not fit returns
  * FA_ERR_UNSUPPORTED.
