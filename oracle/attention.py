@@ -61,19 +61,26 @@ NEG_INF = float("-inf")
 ROW_CHUNK = 1024  # rows per fp64 score block, bounds the memory of one step
 
 __all__ = ["keep_matrix", "head_attention", "attention_forward", "to_bnsd", "from_bnsd",
-           "expand_stats", "NEG_INF"]
+           "expand_stats", "merge_partials", "NEG_INF"]
 
 
 def keep_matrix(rows: torch.Tensor, skv: int, *, mask: Optional[torch.Tensor], causal: bool,
-                pre_tokens: Optional[int], next_tokens: Optional[int]) -> torch.Tensor:
+                pre_tokens: Optional[int], next_tokens: Optional[int], q_start: int = 0,
+                kv_start: int = 0) -> torch.Tensor:
     """Boolean [R, skv]: True where key j is KEPT for query row ``rows[r]``.
 
-    ``mask`` is the [Sq, Skv] slice for this (batch, head), nonzero = excluded.
-    Follows the mask / causal / band readings stated in the module docstring.
+    ``mask`` is the [Sq, Skv] slice for this (batch, head), nonzero = excluded,
+    in the chunk's own coordinates.  ``q_start`` / ``kv_start`` place the
+    chunk's rows and keys in the whole sequence (the V5 page's qStartIdx /
+    kvStartIdx for an outer split): causal and band tests use the global
+    positions i + q_start and j + kv_start.  Follows the mask / causal / band
+    readings stated in the module docstring.
     """
-    i = rows.to(torch.int64).view(-1, 1)
-    j = torch.arange(skv, dtype=torch.int64).view(1, -1)
-    keep = torch.ones(i.shape[0], skv, dtype=torch.bool)
+    il = rows.to(torch.int64).view(-1, 1)
+    jl = torch.arange(skv, dtype=torch.int64).view(1, -1)
+    i = il + int(q_start)
+    j = jl + int(kv_start)
+    keep = torch.ones(il.shape[0], skv, dtype=torch.bool)
     if mask is not None:
         keep &= mask.index_select(0, rows.to(torch.int64)) == 0
     if causal:
@@ -91,7 +98,7 @@ def head_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: 
                    mask: Optional[torch.Tensor] = None, causal: bool = False,
                    pre_tokens: Optional[int] = None, next_tokens: Optional[int] = None,
                    sink: Optional[float] = None, rows: Optional[torch.Tensor] = None,
-                   pse: Optional[torch.Tensor] = None
+                   pse: Optional[torch.Tensor] = None, q_start: int = 0, kv_start: int = 0
                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Attention for one (sequence, query head): q [Sq,D], k [Skv,D], v [Skv,Dv].
 
@@ -122,7 +129,7 @@ def head_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: 
         if pse is not None:
             s = s + pse.index_select(0, r).to(torch.float64)
         keep = keep_matrix(r, skv, mask=mask, causal=causal, pre_tokens=pre_tokens,
-                           next_tokens=next_tokens)
+                           next_tokens=next_tokens, q_start=q_start, kv_start=kv_start)
         s = s.masked_fill(~keep, NEG_INF)
         # m = max(sink, max_j s_ij)
         m = s.amax(dim=1) if skv > 0 else torch.full((r.numel(),), NEG_INF, dtype=torch.float64)
@@ -200,7 +207,7 @@ def attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, layo
                       cu_seqlens_q: Optional[Sequence[int] | torch.Tensor] = None,
                       cu_seqlens_kv: Optional[Sequence[int] | torch.Tensor] = None,
                       samples: Optional[Sequence[Tuple[int, int, torch.Tensor]]] = None,
-                      pse: Optional[torch.Tensor] = None):
+                      pse: Optional[torch.Tensor] = None, q_start: int = 0, kv_start: int = 0):
     """Whole-problem oracle in the caller's layout.
 
     Dense layouts return ``(O, m, l)`` with O in the input layout (last dim Dv)
@@ -213,7 +220,8 @@ def attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, layo
     if layout == "TND":
         return _forward_tnd(q, k, v, scale=scale, q_rope=q_rope, k_rope=k_rope, atten_mask=atten_mask,
                             sink=sink, causal=causal, pre_tokens=pre_tokens, next_tokens=next_tokens,
-                            cu_q=cu_seqlens_q, cu_kv=cu_seqlens_kv, samples=samples, pse=pse)
+                            cu_q=cu_seqlens_q, cu_kv=cu_seqlens_kv, samples=samples, pse=pse,
+                            q_start=q_start, kv_start=kv_start)
     if layout in ("BSH", "SBH"):
         if heads is None:
             raise ValueError("BSH/SBH need the query head count")
@@ -238,7 +246,8 @@ def attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, layo
                               mask=_mask_slice(atten_mask, b, h), causal=causal,
                               pre_tokens=pre_tokens, next_tokens=next_tokens,
                               sink=float(sink[h]) if sink is not None else None, rows=rows,
-                              pse=pse[b if pse.shape[0] > 1 else 0, h] if pse is not None else None)
+                              pse=pse[b if pse.shape[0] > 1 else 0, h] if pse is not None else None,
+                              q_start=q_start, kv_start=kv_start)
 
     if samples is not None:
         return [one(b, h, torch.as_tensor(rows)) for (b, h, rows) in samples]
@@ -257,7 +266,7 @@ def _as_list(cu) -> list:
 
 
 def _forward_tnd(q, k, v, *, scale, q_rope, k_rope, atten_mask, sink, causal, pre_tokens,
-                 next_tokens, cu_q, cu_kv, samples, pse=None):
+                 next_tokens, cu_q, cu_kv, samples, pse=None, q_start=0, kv_start=0):
     if atten_mask is not None and atten_mask.dim() != 2:
         raise NotImplementedError("with TND only a 2-D [Sq, Skv] mask in sequence-local coordinates")
     cq, ck = _as_list(cu_q), _as_list(cu_kv)
@@ -288,7 +297,7 @@ def _forward_tnd(q, k, v, *, scale, q_rope, k_rope, atten_mask, sink, causal, pr
                               mask=atten_mask[:q1 - q0, :k1 - k0] if atten_mask is not None else None,
                               causal=causal, pre_tokens=pre_tokens, next_tokens=next_tokens,
                               sink=float(sink[h]) if sink is not None else None, rows=rows,
-                              pse=pse_block(bi, h))
+                              pse=pse_block(bi, h), q_start=q_start, kv_start=kv_start)
 
     if samples is not None:
         return [one(bi, h, torch.as_tensor(rows)) for (bi, h, rows) in samples]
@@ -315,3 +324,28 @@ def expand_stats(x: torch.Tensor, layout: str, softmax_out_layout: str = "") -> 
     if layout == "TND" and softmax_out_layout == "same_as_input":
         x = x.transpose(0, 1)
     return x.unsqueeze(-1).expand(*x.shape, 8).contiguous()
+
+
+def merge_partials(parts: Sequence[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]]
+                   ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Combine the results of one query chunk against several key chunks.
+
+    Each part is (O_c [..., Dv], m_c [...], l_c [...]) for the same rows, with
+    m_c and l_c the row's max logit and sum of e^(s - m_c) over that chunk's
+    keys (so O_c = sum e^(s - m_c) v / l_c).  Over the union of the chunks the
+    max is m = max_c m_c and, from the definitions of m and l in the sink
+    equations, l = sum_c e^(m_c - m) l_c and O = sum_c e^(m_c - m) l_c O_c / l.
+    Chunks with no kept key (m_c = -inf, l_c = 0) contribute nothing; a row
+    empty in every chunk gets O = 0, m = -inf, l = 0.
+    """
+    Os = [p[0].to(torch.float64) for p in parts]
+    ms = torch.stack([p[1].to(torch.float64) for p in parts])
+    ls = torch.stack([p[2].to(torch.float64) for p in parts])
+    m = ms.amax(dim=0)
+    m_safe = torch.where(torch.isfinite(m), m, torch.zeros_like(m))
+    w = torch.where(torch.isfinite(ms), torch.exp(ms - m_safe) * ls, torch.zeros_like(ls))
+    l = w.sum(dim=0)
+    num = sum(w[c].unsqueeze(-1) * Os[c] for c in range(len(Os)))
+    o = torch.where((l > 0).unsqueeze(-1), num / torch.where(l > 0, l, torch.ones_like(l)).unsqueeze(-1),
+                    torch.zeros_like(num))
+    return o, m, l

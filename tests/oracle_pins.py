@@ -536,4 +536,83 @@ def pin_pse_row_shift_and_neg_inf(orc):
     for x, y, nm in zip(a, b, "Oml"):
         _close(y, x, f"pse -inf as mask {nm}")
 
+
+# ---------------------------------------------------------------------------
+# Outer split: qStartIdx / kvStartIdx offsets and the merge of partial results
+# ---------------------------------------------------------------------------
+
+def pin_outer_split_offsets(orc):
+    """A query / key chunk with global offsets equals SDPA with the global-position causal or band mask."""
+    g = torch.Generator().manual_seed(31)
+    B, N, D = 1, 2, 8
+    q, k, v = _rand((B, N, 23, D), g), _rand((B, N, 17, D), g), _rand((B, N, 17, D), g)
+    sc = 0.4
+    for qs, ks, causal, pre, nxt in [(30, 20, True, None, None), (5, 25, True, None, None),
+                                     (40, 30, False, 6, 3), (0, 0, True, None, None), (12, 3, True, 8, 0)]:
+        mask = None if causal else torch.zeros(23, 17, dtype=torch.uint8)
+        O, M, L = orc.attention_forward(q, k, v, layout="BNSD", scale=sc, causal=causal, atten_mask=mask,
+                                        pre_tokens=pre, next_tokens=nxt, q_start=qs, kv_start=ks)
+        ig = torch.arange(23).view(-1, 1) + qs
+        jg = torch.arange(17).view(1, -1) + ks
+        allow = torch.ones(23, 17, dtype=torch.bool)
+        if causal:
+            allow &= jg <= ig
+        if pre is not None:
+            allow &= (ig - jg) <= pre
+        if nxt is not None:
+            allow &= (jg - ig) <= nxt
+        logits = (sc * q @ k.transpose(-1, -2)).masked_fill(~allow, -math.inf)
+        rows = allow.any(-1)
+        want = F.scaled_dot_product_attention(q, k, v, attn_mask=allow | ~rows.view(-1, 1), scale=sc)
+        want = torch.where(rows.view(1, 1, -1, 1), want, torch.zeros_like(want))
+        tag = f"outer split q_start={qs} kv_start={ks} causal={causal} pre={pre} next={nxt}"
+        _close(O, want, tag + " O")
+        lse = torch.logsumexp(logits, -1)
+        _close(torch.where(rows.view(1, 1, -1), M + torch.log(L), lse), lse, tag + " lse")
+    # an explicit mask stays in the chunk's own coordinates
+    rm = torch.rand(23, 17, generator=g) < 0.3
+    O, _, _ = orc.attention_forward(q, k, v, layout="BNSD", scale=sc, causal=True, atten_mask=rm.to(torch.uint8),
+                                    q_start=30, kv_start=20)
+    allow = ~rm & ((torch.arange(17).view(1, -1) + 20) <= (torch.arange(23).view(-1, 1) + 30))
+    rows = allow.any(-1)
+    want = F.scaled_dot_product_attention(q, k, v, attn_mask=allow | ~rows.view(-1, 1), scale=sc)
+    want = torch.where(rows.view(1, 1, -1, 1), want, torch.zeros_like(want))
+    _close(O, want, "outer split with a chunk-local mask")
+
+
+def pin_outer_split_merge(orc):
+    """Key chunks with kv_start offsets, merged, equal the unsplit call (causal, band, sink in one chunk)."""
+    g = torch.Generator().manual_seed(32)
+    B, N, S, D = 2, 2, 29, 8
+    q, k, v = _rand((B, N, S, D), g), _rand((B, N, S, D), g), _rand((B, N, S, D), g)
+    sink = _rand((N,), g)
+    cuts = [0, 6, 7, 19, 29]
+    for causal, band, use_sink in itertools.product((False, True), (False, True), (False, True)):
+        kw = dict(layout="BNSD", scale=0.5, causal=causal)
+        if band:
+            kw.update(atten_mask=torch.zeros(S, S, dtype=torch.uint8), pre_tokens=5, next_tokens=2)
+        whole = orc.attention_forward(q, k, v, sink=sink if use_sink else None, **kw)
+        parts = []
+        for c in range(len(cuts) - 1):
+            a, b_ = cuts[c], cuts[c + 1]
+            kwc = dict(kw)
+            if band:
+                kwc["atten_mask"] = torch.zeros(S, b_ - a, dtype=torch.uint8)
+            parts.append(orc.attention_forward(q, k[:, :, a:b_], v[:, :, a:b_], kv_start=a,
+                                               sink=sink if (use_sink and c == 1) else None, **kwc))
+        merged = orc.merge_partials(parts)
+        tag = f"merge causal={causal} band={band} sink={use_sink}"
+        for x, y, nm in zip(merged, whole, "Oml"):
+            _close(x, y, f"{tag} {nm}")
+
+
+def pin_offsets_relative_only(orc):
+    """Equal offsets on both sides change nothing: only relative positions enter the window."""
+    g = torch.Generator().manual_seed(33)
+    q, k, v = _rand((1, 2, 21, 8), g), _rand((1, 2, 21, 8), g), _rand((1, 2, 21, 8), g)
+    a = orc.attention_forward(q, k, v, layout="BNSD", scale=0.5, causal=True, pre_tokens=4)
+    b = orc.attention_forward(q, k, v, layout="BNSD", scale=0.5, causal=True, pre_tokens=4, q_start=9, kv_start=9)
+    for x, y, nm in zip(a, b, "Oml"):
+        _close(y, x, f"offsets relative {nm}")
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -38,6 +38,14 @@ MUTANTS = {
     "pse_batch_broadcast": ("pse=pse[b if pse.shape[0] > 1 else 0, h]", "pse=pse[0, h]"),
     "pse_tnd_head_major": ("return pse.reshape(-1)[pse_off[bi]:pse_off[bi + 1]].view(N, lq, lk)[h]",
                            "return pse.reshape(-1)[pse_off[bi]:pse_off[bi + 1]].view(lq, N, lk)[:, h]"),
+    "offset_sign": ("    i = il + int(q_start)\n", "    i = il - int(q_start)\n"),
+    "offset_swapped": ("    j = jl + int(kv_start)\n", "    j = jl + int(q_start)\n"),
+    "offset_on_mask": ("keep &= mask.index_select(0, rows.to(torch.int64)) == 0",
+                       "keep &= mask.index_select(0, (rows.to(torch.int64) + int(q_start)) % mask.shape[0]) == 0"),
+    "merge_drops_l": ("w = torch.where(torch.isfinite(ms), torch.exp(ms - m_safe) * ls, torch.zeros_like(ls))",
+                      "w = torch.where(torch.isfinite(ms), torch.exp(ms - m_safe), torch.zeros_like(ls))"),
+    "merge_sign": ("w = torch.where(torch.isfinite(ms), torch.exp(ms - m_safe) * ls, torch.zeros_like(ls))",
+                   "w = torch.where(torch.isfinite(ms), torch.exp(m_safe - ms) * ls, torch.zeros_like(ls))"),
     "stats_layout_transposed": ("    if layout == \"TND\" and softmax_out_layout == \"same_as_input\":\n        x = x.transpose(0, 1)\n",
                                 "    if layout == \"TND\" and softmax_out_layout == \"\":\n        x = x.transpose(0, 1)\n"),
 }
