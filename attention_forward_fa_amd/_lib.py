@@ -33,7 +33,7 @@ FA_DTYPE = {
     torch.int64: 6,
 }
 
-EXPORTED = ("fa_fwd_get_workspace_size", "fa_fwd", "fa_plan_destroy", "fa_plan_describe",
+EXPORTED = ("fa_fwd_get_workspace_size", "fa_fwd", "fa_fwd_merge", "fa_plan_destroy", "fa_plan_describe",
             "fa_last_error_message")
 
 
@@ -75,7 +75,7 @@ def lib() -> ctypes.CDLL:
         T = P(FaTensor)
         L.fa_fwd_get_workspace_size.restype = ctypes.c_int32
         L.fa_fwd_get_workspace_size.argtypes = [
-            T, T, T, T, T, T, T, T, T, T,
+            T, T, T, T, T, T, T, T, T, T, P(ctypes.c_int64), P(ctypes.c_int64),
             ctypes.c_double, ctypes.c_double, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_char_p,
             T, T, T, P(ctypes.c_uint64), P(ctypes.c_void_p),
@@ -86,6 +86,9 @@ def lib() -> ctypes.CDLL:
         L.fa_plan_destroy.argtypes = [ctypes.c_void_p]
         L.fa_plan_describe.restype = ctypes.c_int32
         L.fa_plan_describe.argtypes = [ctypes.c_void_p, ctypes.c_char_p, ctypes.c_size_t]
+        L.fa_fwd_merge.restype = ctypes.c_int32
+        L.fa_fwd_merge.argtypes = [ctypes.c_int32, T, T, T, ctypes.c_char_p, ctypes.c_int64, ctypes.c_char_p,
+                                   T, T, T, ctypes.c_void_p]
         L.fa_last_error_message.restype = ctypes.c_char_p
         L.fa_last_error_message.argtypes = []
         _lib = L
@@ -121,20 +124,25 @@ def last_error_message() -> str:
 
 
 def fa_fwd_get_workspace_size(query, query_rope, key, key_rope, value, real_shift, atten_mask, sink,
-                              cu_seqlens_q, cu_seqlens_kv, scale_value: float, keep_prob: float,
+                              cu_seqlens_q, cu_seqlens_kv, q_start_idx: Optional[int], kv_start_idx: Optional[int],
+                              scale_value: float, keep_prob: float,
                               pre_tokens: int, next_tokens: int, head_num: int, input_layout: str,
                               inner_precise: int, sparse_mode: int, causal: bool,
                               softmax_out_layout: str, softmax_max, softmax_sum, attention_out,
                               *, device_required: bool = True):
-    """Phase 1.  Tensor arguments are torch tensors or None.  Returns (workspace_bytes, plan handle)."""
+    """Phase 1.  Tensor arguments are torch tensors or None; the start indices
+    are ints or None.  Returns (workspace_bytes, plan handle)."""
     L = lib()
     ds = [describe_tensor(t, device_required=device_required) for t in
           (query, query_rope, key, key_rope, value, real_shift, atten_mask, sink, cu_seqlens_q, cu_seqlens_kv,
            softmax_max, softmax_sum, attention_out)]
+    qs = ctypes.c_int64(int(q_start_idx)) if q_start_idx is not None else None
+    ks = ctypes.c_int64(int(kv_start_idx)) if kv_start_idx is not None else None
     ws = ctypes.c_uint64(0)
     plan = ctypes.c_void_p(None)
     st = L.fa_fwd_get_workspace_size(
-        *(_ref(d) for d in ds[:10]), float(scale_value), float(keep_prob), int(pre_tokens), int(next_tokens),
+        *(_ref(d) for d in ds[:10]), _ref(qs), _ref(ks),
+        float(scale_value), float(keep_prob), int(pre_tokens), int(next_tokens),
         int(head_num), input_layout.encode() if input_layout is not None else None, int(inner_precise),
         int(sparse_mode), 1 if causal else 0,
         softmax_out_layout.encode() if softmax_out_layout is not None else None,
@@ -151,6 +159,23 @@ def fa_fwd(workspace: Optional[torch.Tensor], workspace_size: int, plan, stream:
     st = L.fa_fwd(ptr, int(workspace_size), plan, stream)
     if st != FA_OK:
         raise FaError(st, "fa_fwd", last_error_message())
+
+
+def fa_fwd_merge(part_out, part_max, part_sum, input_layout: str, head_num: int, softmax_out_layout: str,
+                 attention_out, softmax_max, softmax_sum, stream: int) -> None:
+    """Merge partial results (lists of torch tensors) into attention_out / the stats (enqueued on ``stream``)."""
+    L = lib()
+    n = len(part_out)
+    if not (len(part_max) == len(part_sum) == n):
+        raise ValueError("part lists differ in length")
+    arr = lambda ts: (FaTensor * max(n, 1))(*[describe_tensor(t) for t in ts])
+    po, pm, pl = arr(part_out), arr(part_max), arr(part_sum)
+    st = L.fa_fwd_merge(n, po, pm, pl, input_layout.encode(), int(head_num),
+                        softmax_out_layout.encode() if softmax_out_layout is not None else None,
+                        _ref(describe_tensor(attention_out)), _ref(describe_tensor(softmax_max)),
+                        _ref(describe_tensor(softmax_sum)), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_merge", last_error_message())
 
 
 def fa_plan_destroy(plan) -> None:

@@ -49,7 +49,8 @@ class ForwardPlan:
                  query_rope=None, key_rope=None, atten_mask=None, sink=None, cu_seqlens_q=None,
                  cu_seqlens_kv=None, causal: bool = False, pre_tokens: int = UNBOUNDED,
                  next_tokens: int = UNBOUNDED, softmax_out_layout: str = "", out=None,
-                 softmax_max=None, softmax_sum=None, inner_precise: int = 0, real_shift=None):
+                 softmax_max=None, softmax_sum=None, inner_precise: int = 0, real_shift=None,
+                 q_start_idx: Optional[int] = None, kv_start_idx: Optional[int] = None):
         self.device = _check_device(query, key, value, query_rope, key_rope, atten_mask, sink, cu_seqlens_q,
                                     cu_seqlens_kv, out, softmax_max, softmax_sum, real_shift)
         self._keep = (query, key, value, query_rope, key_rope, atten_mask, sink, cu_seqlens_q, cu_seqlens_kv,
@@ -58,7 +59,7 @@ class ForwardPlan:
         self.plan = None
         ws, plan = _lib.fa_fwd_get_workspace_size(
             query, query_rope, key, key_rope, value, real_shift, atten_mask, sink, cu_seqlens_q, cu_seqlens_kv,
-            scale, 1.0, pre_tokens, next_tokens, head_num, layout, inner_precise, 0, causal,
+            q_start_idx, kv_start_idx, scale, 1.0, pre_tokens, next_tokens, head_num, layout, inner_precise, 0, causal,
             softmax_out_layout, softmax_max, softmax_sum, out)
         self.plan = plan
         self.workspace_size = ws
@@ -115,14 +116,17 @@ def attention_forward(query: torch.Tensor, key: torch.Tensor, value: torch.Tenso
                       kv_heads: Optional[int] = None, pre_tokens: int = UNBOUNDED, next_tokens: int = UNBOUNDED,
                       sink: Optional[torch.Tensor] = None, query_rope: Optional[torch.Tensor] = None,
                       key_rope: Optional[torch.Tensor] = None, causal: bool = False,
-                      pse: Optional[torch.Tensor] = None,
+                      pse: Optional[torch.Tensor] = None, q_start_idx: Optional[int] = None,
+                      kv_start_idx: Optional[int] = None,
                       return_softmax_stats: bool = False, return_plan: bool = False):
     """Dense attention forward.
 
     ``layout`` defaults to "BNSD" when ``head_first`` else "BSND"; "BSH" and
     "SBH" need ``heads``.  ``attn_mask``: u8/bool, nonzero = excluded.
     ``pse``: optional additive bias [B|1, N, Sq, Skv] in the query's dtype,
-    added after the scale (the realShift input).
+    added after the scale (the realShift input).  ``q_start_idx`` /
+    ``kv_start_idx``: where these query / key rows start in the whole sequence
+    (outer split); causal and window tests then use global positions.
     ``scale`` defaults to D**-0.5 with D the non-rope head dim.  Returns the
     output, plus (softmax_max, softmax_sum) shaped [B,N,Sq,8] when
     ``return_softmax_stats``.
@@ -143,7 +147,8 @@ def attention_forward(query: torch.Tensor, key: torch.Tensor, value: torch.Tenso
         ssum = torch.empty_like(smax)
     plan = ForwardPlan(query, key, value, layout=layout, scale=scale, head_num=n, query_rope=query_rope,
                        key_rope=key_rope, atten_mask=attn_mask, sink=sink, causal=causal, pre_tokens=pre_tokens,
-                       next_tokens=next_tokens, out=out, softmax_max=smax, softmax_sum=ssum, real_shift=pse)
+                       next_tokens=next_tokens, out=out, softmax_max=smax, softmax_sum=ssum, real_shift=pse,
+                       q_start_idx=q_start_idx, kv_start_idx=kv_start_idx)
     plan.run()
     if return_plan:
         return plan
@@ -161,7 +166,8 @@ def attention_forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
                              q_rope: Optional[torch.Tensor] = None, k_rope: Optional[torch.Tensor] = None,
                              atten_mask: Optional[torch.Tensor] = None, pre_tokens: int = UNBOUNDED,
                              next_tokens: int = UNBOUNDED, softmax_out_layout: str = "",
-                             pse: Optional[torch.Tensor] = None,
+                             pse: Optional[torch.Tensor] = None, q_start_idx: Optional[int] = None,
+                             kv_start_idx: Optional[int] = None,
                              return_softmax_stats: bool = False, return_plan: bool = False):
     """Varlen (TND) attention forward over sequences packed along T.
 
@@ -193,7 +199,7 @@ def attention_forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
                        atten_mask=atten_mask, sink=sink, cu_seqlens_q=cu_seqlens_q, cu_seqlens_kv=cu_seqlens_k,
                        causal=causal, pre_tokens=pre_tokens, next_tokens=next_tokens,
                        softmax_out_layout=softmax_out_layout, out=out, softmax_max=smax, softmax_sum=ssum,
-                       real_shift=pse)
+                       real_shift=pse, q_start_idx=q_start_idx, kv_start_idx=kv_start_idx)
     plan.run()
     if return_plan:
         return plan
@@ -201,6 +207,18 @@ def attention_forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
     if return_softmax_stats:
         return out, smax, ssum
     return out
+
+
+def merge_partials(parts, *, layout: str, heads: int, softmax_out_layout: str = ""):
+    """Merge [(out, softmax_max, softmax_sum), ...] of one query chunk over several key
+    chunks into (out, softmax_max, softmax_sum) over all keys (``fa_fwd_merge``)."""
+    o0, m0, _ = parts[0]
+    out = torch.empty_like(o0)
+    smax = torch.empty_like(m0)
+    ssum = torch.empty_like(m0)
+    _lib.fa_fwd_merge([p[0] for p in parts], [p[1] for p in parts], [p[2] for p in parts], layout, heads,
+                      softmax_out_layout, out, smax, ssum, _stream_handle(out.device))
+    return out, smax, ssum
 
 
 def cu_from_actual_seq_len(actual) -> list:

@@ -28,7 +28,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Xclang", 
              "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 
-HIP_SOURCES = ["fa_launch.hip", "fa_mfma_bf16.hip", "fa_mfma_f16.hip", "fa_generic.hip"]
+HIP_SOURCES = ["fa_launch.hip", "fa_mfma_bf16.hip", "fa_mfma_f16.hip", "fa_generic.hip", "fa_merge.hip"]
 # Extra flags per source.  The matrix-core kernel never produces NaN from
 # finite inputs, so max needs no NaN canonicalisation.
 PER_SOURCE_FLAGS = {"fa_mfma_bf16.hip": ["-fno-honor-nans"], "fa_mfma_f16.hip": ["-fno-honor-nans"]}

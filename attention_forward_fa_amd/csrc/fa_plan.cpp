@@ -15,6 +15,7 @@
 
 #include "fa_fwd.h"
 #include "fa_params.h"
+#include "fa_merge.h"
 #include "fa_plan.h"
 
 namespace {
@@ -146,7 +147,8 @@ extern "C" int32_t fa_plan_describe(const fa_plan* plan, char* buf, size_t len) 
 extern "C" fa_status fa_fwd_get_workspace_size(
     const fa_tensor* query, const fa_tensor* query_rope, const fa_tensor* key, const fa_tensor* key_rope,
     const fa_tensor* value, const fa_tensor* real_shift, const fa_tensor* atten_mask, const fa_tensor* sink,
-    const fa_tensor* cu_seqlens_q, const fa_tensor* cu_seqlens_kv, double scale_value, double keep_prob,
+    const fa_tensor* cu_seqlens_q, const fa_tensor* cu_seqlens_kv, const int64_t* q_start_idx,
+    const int64_t* kv_start_idx, double scale_value, double keep_prob,
     int64_t pre_tokens, int64_t next_tokens, int64_t head_num, const char* input_layout, int64_t inner_precise,
     int64_t sparse_mode, int32_t causal, const char* softmax_out_layout, const fa_tensor* softmax_max,
     const fa_tensor* softmax_sum, const fa_tensor* attention_out, uint64_t* workspace_size, fa_plan** plan) {
@@ -321,6 +323,15 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   if (causal && nxt > 0) nxt = 0;
   if (band && pre + nxt < 0)
     return fail(FA_ERR_UNSUPPORTED, "preTokens + nextTokens < 0: the window is empty");
+  // Outer split: the chunk's rows start at q_start and its keys at kv_start
+  // in the whole sequence, and the window is a condition on global positions:
+  // -pre <= (j + kv_start) - (i + q_start) <= next, i.e. the same test on
+  // local positions with both bounds moved by q_start - kv_start.
+  const int64_t qs = q_start_idx ? *q_start_idx : 0, ks = kv_start_idx ? *kv_start_idx : 0;
+  if (qs < 0 || ks < 0 || qs > ((int64_t)1 << 26) || ks > ((int64_t)1 << 26))
+    return fail(FA_ERR_UNSUPPORTED, "q_start_idx / kv_start_idx must be in [0, 2^26]");
+  pre = clamp_window(pre - (qs - ks));
+  nxt = clamp_window(nxt + (qs - ks));
 
   // ---- kernel choice
   fa_plan* pl = new (std::nothrow) fa_plan();
@@ -477,5 +488,103 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   p.num_wg = (int32_t)wg;
   *workspace_size = pl->ws_bytes;
   *plan = pl;
+  return FA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Merge of partial results (outer split along the keys)
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// Strides (batch, head, row) of an [..., 8] statistics tensor for layout L.
+fa_status stats_view(const fa_tensor* s, Layout L, bool same_as_input, const View& o, const char* nm, int64_t* sb,
+                     int64_t* sh, int64_t* ss) {
+  if (s->dtype != FA_DTYPE_F32) return fail(FA_ERR_PARAM_INVALID, "%s must be f32", nm);
+  if (L == L_TND) {
+    if (s->ndim != 3 || s->shape[2] != 8) return fail(FA_ERR_UNSUPPORTED, "%s must be [N,T,8] or [T,N,8]", nm);
+    if (same_as_input) {
+      if (s->shape[0] != o.s || s->shape[1] != o.n) return fail(FA_ERR_UNSUPPORTED, "%s must be [T,N,8]", nm);
+      *sb = 0; *ss = s->stride[0]; *sh = s->stride[1];
+    } else {
+      if (s->shape[0] != o.n || s->shape[1] != o.s) return fail(FA_ERR_UNSUPPORTED, "%s must be [N,T,8]", nm);
+      *sb = 0; *sh = s->stride[0]; *ss = s->stride[1];
+    }
+  } else {
+    if (s->ndim != 4 || s->shape[0] != o.b || s->shape[1] != o.n || s->shape[2] != o.s || s->shape[3] != 8)
+      return fail(FA_ERR_UNSUPPORTED, "%s must be [B,N,Sq,8]", nm);
+    *sb = s->stride[0]; *sh = s->stride[1]; *ss = s->stride[2];
+  }
+  if (s->stride[s->ndim - 1] != 1) return fail(FA_ERR_PARAM_INVALID, "%s: last dimension must be contiguous", nm);
+  if (!s->data) return fail(FA_ERR_PARAM_NULLPTR, "%s data is NULL", nm);
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" fa_status fa_fwd_merge(int32_t n_parts, const fa_tensor* part_out, const fa_tensor* part_max,
+                                  const fa_tensor* part_sum, const char* input_layout, int64_t head_num,
+                                  const char* softmax_out_layout, const fa_tensor* attention_out,
+                                  const fa_tensor* softmax_max, const fa_tensor* softmax_sum, void* stream) {
+  if (!part_out || !part_max || !part_sum) return fail(FA_ERR_PARAM_NULLPTR, "part arrays are NULL");
+  if (!attention_out || !input_layout) return fail(FA_ERR_PARAM_NULLPTR, "attention_out / input_layout is NULL");
+  if (n_parts < 1 || n_parts > fa::kMergeMaxParts)
+    return fail(FA_ERR_UNSUPPORTED, "n_parts %d outside 1..%d", n_parts, fa::kMergeMaxParts);
+  const Layout L = parse_layout(input_layout);
+  if (L == L_BAD) return fail(FA_ERR_PARAM_INVALID, "input_layout '%s' not one of BNSD BSND BSH SBH TND", input_layout);
+  const char* sol = softmax_out_layout ? softmax_out_layout : "";
+  const bool same = !strcmp(sol, "same_as_input");
+  if (!same && sol[0] != '\0') return fail(FA_ERR_PARAM_INVALID, "softmax_out_layout '%s' invalid", sol);
+  const int32_t dt = attention_out->dtype;
+  if (dt != FA_DTYPE_F32 && dt != FA_DTYPE_F16 && dt != FA_DTYPE_BF16)
+    return fail(FA_ERR_PARAM_INVALID, "attention_out dtype %s not f32/f16/bf16", dtype_name(dt));
+  if (head_num <= 0 || head_num > 256) return fail(FA_ERR_UNSUPPORTED, "head_num outside 1..256");
+  fa_status st;
+  View o;
+  if ((st = decode(attention_out, L, "attention_out", head_num, 0, &o))) return st;
+  if (o.d > 256 || o.n != head_num) return fail(FA_ERR_UNSUPPORTED, "attention_out heads / dim out of range");
+  if (!attention_out->data) return fail(FA_ERR_PARAM_NULLPTR, "attention_out data is NULL");
+  fa::MergeParams mp{};
+  mp.nparts = n_parts;
+  mp.dv = (int32_t)o.d;
+  mp.nbatch = (int32_t)o.b;
+  mp.nheads = (int32_t)o.n;
+  mp.nrows = (int32_t)o.s;
+  mp.o = attention_out->data;
+  mp.o_sb = o.sb; mp.o_ss = o.ss; mp.o_sh = o.sh;
+  for (int c = 0; c < n_parts; ++c) {
+    View pv;
+    if (part_out[c].dtype != dt) return fail(FA_ERR_PARAM_INVALID, "part %d output dtype differs", c);
+    if ((st = decode(&part_out[c], L, "part output", head_num, 0, &pv))) return st;
+    if (pv.b != o.b || pv.s != o.s || pv.n != o.n || pv.d != o.d)
+      return fail(FA_ERR_UNSUPPORTED, "part %d output shape differs from attention_out", c);
+    if (!part_out[c].data) return fail(FA_ERR_PARAM_NULLPTR, "part %d output data is NULL", c);
+    mp.po[c] = part_out[c].data;
+    mp.po_sb[c] = pv.sb; mp.po_ss[c] = pv.ss; mp.po_sh[c] = pv.sh;
+    int64_t sb, sh, ss, sb2, sh2, ss2;
+    if ((st = stats_view(&part_max[c], L, same, o, "part softmax_max", &sb, &sh, &ss))) return st;
+    if ((st = stats_view(&part_sum[c], L, same, o, "part softmax_sum", &sb2, &sh2, &ss2))) return st;
+    if (sb != sb2 || sh != sh2 || ss != ss2) return fail(FA_ERR_UNSUPPORTED, "part %d stats strides differ", c);
+    mp.pm[c] = static_cast<const float*>(part_max[c].data);
+    mp.pl[c] = static_cast<const float*>(part_sum[c].data);
+    mp.pst_sb[c] = sb; mp.pst_sh[c] = sh; mp.pst_ss[c] = ss;
+  }
+  mp.st_sb = mp.st_sh = mp.st_ss = 0;
+  if (softmax_max || softmax_sum) {
+    int64_t sb = 0, sh = 0, ss = 0, sb2 = 0, sh2 = 0, ss2 = 0;
+    if (softmax_max && (st = stats_view(softmax_max, L, same, o, "softmax_max", &sb, &sh, &ss))) return st;
+    if (softmax_sum && (st = stats_view(softmax_sum, L, same, o, "softmax_sum", &sb2, &sh2, &ss2))) return st;
+    if (softmax_max && softmax_sum && (sb != sb2 || sh != sh2 || ss != ss2))
+      return fail(FA_ERR_UNSUPPORTED, "softmax_max and softmax_sum must have equal strides");
+    if (!softmax_max) { sb = sb2; sh = sh2; ss = ss2; }
+    mp.st_sb = sb; mp.st_sh = sh; mp.st_ss = ss;
+  }
+  mp.m = softmax_max ? static_cast<float*>(softmax_max->data) : nullptr;
+  mp.l = softmax_sum ? static_cast<float*>(softmax_sum->data) : nullptr;
+  const int e = fa::merge_launch(mp, dt, stream);
+  if (e != 0) {
+    fail(FA_ERR_RUNTIME, "merge kernel launch failed (HIP error %d)", e);
+    return FA_ERR_RUNTIME;
+  }
   return FA_OK;
 }

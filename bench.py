@@ -259,7 +259,7 @@ def main():
         # phase 1 + phase 2; the workspace is allocated once, outside the timed region
         wsz, h = _lib.fa_fwd_get_workspace_size(
             g["q"], g["q_rope"], g["k"], g["k_rope"], g["v"], g["pse"], g["atten_mask"], g["sink"], g["cu_seqlens_q"],
-            g["cu_seqlens_kv"], case.scale, 1.0, case.pre_tokens, case.next_tokens, nheads, case.layout, 0, 0,
+            g["cu_seqlens_kv"], None, None, case.scale, 1.0, case.pre_tokens, case.next_tokens, nheads, case.layout, 0, 0,
             case.causal, case.softmax_out_layout, smax, ssum, out)
         if ev_pair is not None:
             ev_pair[0].record(stream)

@@ -118,6 +118,14 @@ typedef int32_t fa_status;
  *                       I32 [B+1], cumulative lengths with a leading 0,
  *                       non-decreasing, last entry == T of q / k.  Read by the
  *                       device in phase 2 only; zero-length sequences allowed.
+ *   q_start_idx, kv_start_idx  optional HOST pointers to one int64 each (NULL
+ *                       = 0): where this call's query rows and key rows start
+ *                       in the whole sequence, for an outer split along the
+ *                       sequence (V5 parameter table, rows qStartIdxOptional /
+ *                       kvStartIdxOptional).  The causal and preTokens /
+ *                       nextTokens tests then use global positions
+ *                       i + q_start_idx and j + kv_start_idx; atten_mask stays
+ *                       in the call's own coordinates.  Each in [0, 2^26].
  *   scale_value         finite, >= 0; multiplies both score terms.
  *   keep_prob           must be 1.0 (no dropout).
  *   pre_tokens, next_tokens  window: key j is kept for row i iff
@@ -165,7 +173,8 @@ fa_status fa_fwd_get_workspace_size(
     const fa_tensor* query, const fa_tensor* query_rope, const fa_tensor* key,
     const fa_tensor* key_rope, const fa_tensor* value, const fa_tensor* real_shift,
     const fa_tensor* atten_mask, const fa_tensor* sink, const fa_tensor* cu_seqlens_q,
-    const fa_tensor* cu_seqlens_kv, double scale_value, double keep_prob, int64_t pre_tokens,
+    const fa_tensor* cu_seqlens_kv, const int64_t* q_start_idx, const int64_t* kv_start_idx,
+    double scale_value, double keep_prob, int64_t pre_tokens,
     int64_t next_tokens, int64_t head_num, const char* input_layout, int64_t inner_precise,
     int64_t sparse_mode, int32_t causal, const char* softmax_out_layout,
     const fa_tensor* softmax_max, const fa_tensor* softmax_sum, const fa_tensor* attention_out,
@@ -183,6 +192,37 @@ fa_status fa_fwd_get_workspace_size(
  * FA_ERR_RUNTIME.  The plan is not consumed.
  */
 fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_plan* plan, void* stream);
+
+/*
+ * Merge the results of one query chunk computed against several key chunks
+ * (an outer split along the key sequence: one fa_fwd call per chunk with its
+ * kv_start_idx, the sink given to one call only) into the result over all
+ * keys.  With m_c, l_c the statistics of part c and O_c its output:
+ *     m = max_c m_c,  w_c = e^(m_c - m) l_c,  l = sum_c w_c,
+ *     O = sum_c w_c O_c / l
+ * (from the definitions of softmaxMax / softmaxSum in the sink equations of
+ * the V5 page, 功能说明 -> 计算公式).  Parts with m_c = -inf weigh nothing;
+ * rows empty in every part get O = 0, m = -inf, l = 0.
+ *
+ *   n_parts             1..16.
+ *   part_out            host array of n_parts descriptors, each shaped like
+ *                       attention_out (same dtype, layout and sizes).
+ *   part_max, part_sum  host arrays of n_parts F32 statistics descriptors in
+ *                       the forward's statistics layout (required).
+ *   input_layout, head_num, softmax_out_layout  as for phase 1.
+ *   attention_out       merged output (F32, F16 or BF16).  It may be one of
+ *                       the parts only if every part is read before it is
+ *                       written: each row is read and written by one
+ *                       wavefront, so aliasing a part row-for-row is safe.
+ *   softmax_max, softmax_sum  optional merged statistics (NULL = not written).
+ *   stream              hipStream_t; asynchronous, no workspace.
+ * Returns FA_OK, FA_ERR_PARAM_NULLPTR, FA_ERR_PARAM_INVALID,
+ * FA_ERR_UNSUPPORTED or FA_ERR_RUNTIME.
+ */
+fa_status fa_fwd_merge(int32_t n_parts, const fa_tensor* part_out, const fa_tensor* part_max,
+                       const fa_tensor* part_sum, const char* input_layout, int64_t head_num,
+                       const char* softmax_out_layout, const fa_tensor* attention_out,
+                       const fa_tensor* softmax_max, const fa_tensor* softmax_sum, void* stream);
 
 /* Release a plan from phase 1.  NULL is ignored. */
 void fa_plan_destroy(fa_plan* plan);

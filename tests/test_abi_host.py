@@ -38,7 +38,7 @@ def desc(shape, dtype=BF16, strides=None, addr=ADDR):
 
 def plan(q, k, v, o, *, qr=None, kr=None, pse=None, mask=None, sink=None, cuq=None, cuk=None, scale=0.088,
          keep=1.0, pre=2**31 - 1, nxt=2**31 - 1, heads=None, layout=b"BSND", inner=0, sparse=0, causal=0,
-         sol=b"", smax=None, ssum=None):
+         sol=b"", smax=None, ssum=None, qs=None, ks=None):
     L = _lib.lib()
     ws = ctypes.c_uint64(123)
     pl = ctypes.c_void_p(None)
@@ -46,7 +46,10 @@ def plan(q, k, v, o, *, qr=None, kr=None, pse=None, mask=None, sink=None, cuq=No
     if heads is None:
         axis = {b"BNSD": 1, b"BSND": 2, b"TND": 1}.get(layout)
         heads = q.shape[axis] if (q is not None and axis is not None) else 24
+    qsv = ctypes.c_int64(qs) if qs is not None else None
+    ksv = ctypes.c_int64(ks) if ks is not None else None
     st = L.fa_fwd_get_workspace_size(r(q), r(qr), r(k), r(kr), r(v), r(pse), r(mask), r(sink), r(cuq), r(cuk),
+                                     r(qsv), r(ksv),
                                      scale, keep, pre, nxt, heads, layout, inner, sparse, causal, sol, r(smax),
                                      r(ssum), r(o), ctypes.byref(ws), ctypes.byref(pl))
     return st, ws.value, pl.value
@@ -153,11 +156,11 @@ def test_null_layout_and_outputs():
     ws = ctypes.c_uint64(0)
     pl = ctypes.c_void_p(None)
     r = ctypes.byref
-    st = L.fa_fwd_get_workspace_size(r(q), None, r(k), None, r(v), None, None, None, None, None, 0.1, 1.0, 0, 0,
-                                     24, None, 0, 0, 0, b"", None, None, r(o), r(ws), r(pl))
+    st = L.fa_fwd_get_workspace_size(r(q), None, r(k), None, r(v), None, None, None, None, None, None, None, 0.1,
+                                     1.0, 0, 0, 24, None, 0, 0, 0, b"", None, None, r(o), r(ws), r(pl))
     assert st == 161001
-    st = L.fa_fwd_get_workspace_size(r(q), None, r(k), None, r(v), None, None, None, None, None, 0.1, 1.0, 0, 0,
-                                     24, b"BSND", 0, 0, 0, b"", None, None, r(o), None, r(pl))
+    st = L.fa_fwd_get_workspace_size(r(q), None, r(k), None, r(v), None, None, None, None, None, None, None, 0.1,
+                                     1.0, 0, 0, 24, b"BSND", 0, 0, 0, b"", None, None, r(o), None, r(pl))
     assert st == 161001
 
 
@@ -434,3 +437,42 @@ def test_pse_tnd_workspace():
     _lib.fa_plan_destroy(pl)
     st, _, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND", pse=desc([10, 10]))
     assert st == 561103 and pl is None
+
+
+# ---------------------------------------------------------------------------
+# outer split (q_start_idx / kv_start_idx) and the merge entry point
+# ---------------------------------------------------------------------------
+
+def test_outer_split_moves_the_window():
+    q = desc([1, 2, 512, 128])
+    # causal chunk whose keys all precede its rows: the window no longer cuts
+    st, _, pl = plan(q, q, q, q, layout=b"BNSD", causal=1, qs=4096, ks=0)
+    assert st == 0, _lib.last_error_message()
+    d = describe(pl)
+    assert "pre=268431360" in d and "next=4096" in d and "reverse=0" in d, d
+    _lib.fa_plan_destroy(pl)
+    st, _, pl = plan(q, q, q, q, layout=b"BNSD", causal=1, pre=100, qs=1000, ks=1200)
+    assert st == 0 and "pre=300 " in describe(pl) and "next=-200 " in describe(pl), describe(pl)
+    _lib.fa_plan_destroy(pl)
+    st, _, pl = plan(q, q, q, q, layout=b"BNSD", causal=1, qs=-1)
+    assert st == 561103 and pl is None
+
+
+def _merge_call(parts, out, smax=None, ssum=None, layout=b"BNSD", heads=2, sol=b""):
+    L = _lib.lib()
+    n = len(parts)
+    arr = lambda i: (_lib.FaTensor * n)(*[p[i] for p in parts])
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    return L.fa_fwd_merge(n, arr(0), arr(1), arr(2), layout, heads, sol, r(out), r(smax), r(ssum), None)
+
+
+def test_merge_validation():
+    o = desc([1, 2, 64, 128])
+    st_ = desc([1, 2, 64, 8], F32)
+    part = (o, st_, st_)
+    assert _merge_call([part] * 17, o) == 561103                       # too many parts
+    assert _merge_call([(desc([1, 2, 63, 128]), st_, st_)], o) == 561103  # shape differs
+    assert _merge_call([(o, desc([1, 2, 64, 4], F32), st_)], o) == 561103  # stats shape
+    assert _merge_call([(o, desc([1, 2, 64, 8], BF16), st_)], o) == 161002  # stats dtype
+    assert _merge_call([(desc([1, 2, 64, 128], F16), st_, st_)], o) == 161002  # out dtype differs
+    assert _merge_call([part], o, layout=b"XYZ") == 161002

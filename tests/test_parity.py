@@ -301,3 +301,88 @@ def test_full_size_sampled(name):
     assert torch.isfinite(o.float()).all()
     assert bool((smax == smax[..., :1]).all()) and bool((ssum == ssum[..., :1]).all())
     assert bool((ssum[..., 0] >= 1.0 - 1e-6).all())
+
+
+# ---------------------------------------------------------------------------
+# outer split: key chunks with kv_start_idx, merged on the GPU
+# ---------------------------------------------------------------------------
+
+def _chunk_case(case, a, b):
+    """The same problem restricted to keys [a, b) (BNSD)."""
+    import copy
+    c = copy.copy(case)
+    c.k, c.v = case.k[:, :, a:b].contiguous(), case.v[:, :, a:b].contiguous()
+    if case.atten_mask is not None:
+        c.atten_mask = case.atten_mask[:, a:b].contiguous()
+    if case.pse is not None:
+        c.pse = case.pse[..., a:b].contiguous()
+    return c
+
+
+def _gpu_forward(case, *, q_start=None, kv_start=None, sink=True):
+    g = {k: (v.to("cuda:0") if v is not None else None) for k, v in case.tensors().items()}
+    res = api.attention_forward(g["q"], g["k"], g["v"], attn_mask=g["atten_mask"], scale=case.scale,
+                                layout=case.layout, pre_tokens=case.pre_tokens, next_tokens=case.next_tokens,
+                                sink=g["sink"] if sink else None, causal=case.causal, pse=g["pse"],
+                                q_start_idx=q_start, kv_start_idx=kv_start, return_softmax_stats=True)
+    return res
+
+
+OUTER = {
+    "causal": lambda: synth.dense_case("x", "BNSD", 1, 2, 500, 128, "bf16", 80, causal=True),
+    "band_mask": lambda: _band_mask_case(81, 60, 5),
+    "sink_causal_fp16": lambda: synth.dense_case("x", "BNSD", 2, 2, 300, 128, "fp16", 82, causal=True, sink=True),
+    "pse_full": lambda: synth.dense_case("x", "BNSD", 1, 2, 260, 128, "bf16", 83, pse="full", causal=True),
+    "fp32_causal": lambda: synth.dense_case("x", "BNSD", 1, 2, 150, 64, "fp32", 84, causal=True),
+}
+
+
+@pytest.mark.parametrize("kernel", ["auto", "mfma", "generic"])
+@pytest.mark.parametrize("name", sorted(OUTER))
+def test_outer_split_merge(name, kernel):
+    case = OUTER[name]()
+    if kernel == "mfma" and case.q.dtype == torch.float32:
+        pytest.skip("the matrix-core kernels take f16 / bf16 only")
+    S = case.k.shape[2]
+    cuts = [0, S // 4 + 3, S // 4 + 4, (3 * S) // 5, S]
+    print(f"[parity] outer split {name} kernel={kernel} cuts={cuts}", flush=True)
+    parts = []
+    with pu.forced_kernel(kernel):
+        for c in range(len(cuts) - 1):
+            a, b = cuts[c], cuts[c + 1]
+            ch = _chunk_case(case, a, b)
+            # one chunk per call; the sink goes to exactly one of them
+            parts.append(_gpu_forward(ch, kv_start=a, sink=(c == 0)))
+            if c == 1:  # each chunk on its own against the oracle with the same offset
+                o1, m1, l1 = (x.cpu() for x in parts[-1])
+                O, M, L = orc.attention_forward(ch.q, ch.k, ch.v, layout="BNSD", scale=ch.scale,
+                                                atten_mask=ch.atten_mask, causal=ch.causal, pse=ch.pse,
+                                                pre_tokens=ch.pre_tokens, next_tokens=ch.next_tokens,
+                                                kv_start=a)
+                pu.check_output(o1, O, case.q.dtype, "chunk O")
+                pu.check_stats(m1, M, "max", case.q.dtype)
+                pu.check_stats(l1, L, "sum", case.q.dtype)
+        o, smax, ssum = api.merge_partials(parts, layout="BNSD", heads=case.q.shape[1])
+        torch.cuda.synchronize()
+    O, M, L = pu.run_oracle(case)
+    dt = case.q.dtype
+    errs = {"O": pu.check_output(o.cpu(), O, dt), "m": pu.check_stats(smax.cpu(), M, "max", dt),
+            "logl": pu.check_stats(ssum.cpu(), L, "sum", dt)}
+    _report(f"outer/{name}/{kernel}", errs)
+
+
+@pytest.mark.parametrize("kernel", ["auto", "generic"])
+def test_outer_split_query_chunk(kernel):
+    """Rows [r0, S) with q_start_idx = r0 against all keys equal those rows of the whole causal result."""
+    case = synth.dense_case("x", "BNSD", 1, 2, 400, 128, "bf16", 85, causal=True, sink=True)
+    r0 = 137
+    import copy
+    ch = copy.copy(case)
+    ch.q = case.q[:, :, r0:].contiguous()
+    with pu.forced_kernel(kernel):
+        o, smax, ssum = (x.cpu() for x in _gpu_forward(ch, q_start=r0))
+    O, M, L = pu.run_oracle(case)
+    dt = case.q.dtype
+    pu.check_output(o, O[:, :, r0:], dt, "query chunk O")
+    pu.check_stats(smax, M[:, :, r0:], "max", dt)
+    pu.check_stats(ssum, L[:, :, r0:], "sum", dt)
