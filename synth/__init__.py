@@ -180,7 +180,11 @@ def varlen_case(name: str, lengths_q: Sequence[int], nq: int, d: int, dtype: str
 # ---------------------------------------------------------------------------
 
 WORKLOADS = ("c1_fp32_bnsd", "c2_dense_bsnd", "c3_causal", "c3_band", "c4_varlen_causal",
-             "c5_varlen_sink_rope", "c6_dense_pse")
+             "c5_varlen_sink_rope", "c6_dense_pse", "c7_outer_split")
+
+# The c7 workload runs the c2 problem as an outer split: its keys in these
+# chunks, one forward call per chunk (with its kv start), then the merge.
+C7_CUTS = (0, 2048, 4096)
 
 
 def c4_lengths(seed: int = 4, n: int = 16, total: int = 8192) -> List[int]:
@@ -209,6 +213,9 @@ def workload(name: str, dtype: str = "bf16", small: bool = False) -> Case:
                                sink=True, causal=True, scale=128 ** -0.5)
         return varlen_case(name, [2048] * 8, 64, 128, "bf16", seed=5, drope=64, sink=True,
                            causal=True, scale=128 ** -0.5)
+    if name == "c7_outer_split":
+        s = 4096 if not small else 320
+        return dense_case(name, "BSND", 2, 24 if not small else 3, s, 128, "bf16", seed=2)
     if name == "c6_dense_pse":
         # the additive bias term: a full [B, N, S, S] pse makes the pass HBM-bound
         s = 4096 if not small else 300
