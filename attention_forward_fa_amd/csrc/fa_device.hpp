@@ -111,6 +111,38 @@ __device__ __forceinline__ void key_range(const Params& p, int i_first, int i_la
   *hi = e;
 }
 
+// This tile's row of mask block classes (kClsRows query rows starting at
+// row0 of the sequence), or null when the rows lie outside the 2-D TND mask.
+__device__ __forceinline__ const uint8_t* mask_class_row(const Params& p, const Tile& tl, int row0) {
+  if (!p.has_mask || p.mask_cls == nullptr) return nullptr;
+  const int t = row0 / kClsRows;
+  if (t >= p.cls_tiles) return nullptr;
+  int64_t slice = 0;
+  if (!p.varlen) {
+    const int mb = p.m_sb != 0 ? tl.b : 0, mh = p.m_sh != 0 ? tl.h : 0;
+    slice = (int64_t)mb * p.cls_nh + mh;
+  }
+  return p.mask_cls + (slice * p.cls_tiles + t) * p.cls_kblocks;
+}
+
+// Class of the key block starting at jb for a class row (see mask_class_row).
+// The row pointer and jb are the same in every lane of a wave; the table does
+// not change while a forward kernel runs, so the byte comes in through a
+// scalar load of its aligned dword (the table is padded to 16 bytes), which
+// leaves the vector memory counters to the key/value staging.
+__device__ __forceinline__ int mask_class(const Params& p, const uint8_t* cls_row, int jb) {
+  if (!p.has_mask) return CLS_KEPT;
+  const int kb = jb / kClsKeys;
+  if (cls_row == nullptr || kb >= p.cls_kblocks) return CLS_EXCLUDED;  // outside the 2-D TND mask
+  const uint64_t a = reinterpret_cast<uint64_t>(cls_row) + (uint64_t)kb;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint64_t au = ((uint64_t)hi << 32) | lo;
+  using const_u32 = const __attribute__((address_space(4))) uint32_t;
+  const uint32_t w = *reinterpret_cast<const_u32*>(au & ~(uint64_t)3);
+  return (int)((w >> (8 * (lo & 3u))) & 0xffu);
+}
+
 // Element index of the pse value for (row, key 0) of this tile's (sequence,
 // head): dense [B|1, N, Sq, Skv] by strides; TND from the sequence's block
 // [N, Sq_b, Skv_b] in the flat tensor.  Reads add the key and stay below

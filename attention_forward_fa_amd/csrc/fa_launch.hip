@@ -68,6 +68,39 @@ __global__ void __launch_bounds__(256) varlen_pse_prefix(const int32_t* __restri
   if (nbatch == 0 && tid == 0) off[0] = 0;
 }
 
+// Mask block classes: one workgroup per (slice, 128-row tile, 64-key block).
+// A position counts when it lies inside [rows, cols); for the 2-D TND mask
+// (outside_excluded) positions beyond it count as excluded, as the kernels
+// read them.  Class: all counted positions kept, all excluded, or mixed.
+__global__ void __launch_bounds__(256) mask_classify(const uint8_t* __restrict__ mask, int64_t m_sb, int64_t m_sh,
+                                                     int64_t m_sq, int64_t m_sk, int nh, int rows, int cols,
+                                                     int tiles, int kblocks, int outside_excluded,
+                                                     uint8_t* __restrict__ cls) {
+  const int64_t id = blockIdx.x;
+  const int kb = (int)(id % kblocks);
+  const int t = (int)((id / kblocks) % tiles);
+  const int64_t slice = id / ((int64_t)kblocks * tiles);
+  const int mb = (int)(slice / nh), mh = (int)(slice % nh);
+  const uint8_t* base = mask + mb * m_sb + mh * m_sh;
+  // thread: row tid / 2 of the tile, keys 32 (tid % 2) .. +31 of the block
+  const int r = t * kClsRows + (threadIdx.x >> 1);
+  const int c0 = kb * kClsKeys + 32 * (threadIdx.x & 1);
+  bool kept = false, excl = false;
+  for (int c = c0; c < c0 + 32; ++c) {
+    const bool inside = r < rows && c < cols;
+    if (inside) {
+      const bool e = base[(int64_t)r * m_sq + (int64_t)c * m_sk] != 0;
+      kept |= !e;
+      excl |= e;
+    } else if (outside_excluded) {
+      excl = true;
+    }
+  }
+  const int any_kept = __syncthreads_or(kept);
+  const int any_excl = __syncthreads_or(excl);
+  if (threadIdx.x == 0) cls[id] = any_kept ? (any_excl ? CLS_MIXED : CLS_KEPT) : CLS_EXCLUDED;
+}
+
 }  // namespace fa
 
 namespace {
@@ -94,20 +127,38 @@ extern "C" fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_p
     return FA_ERR_WORKSPACE;
   }
   fa::Params p = plan->p;
-  if (p.varlen && p.has_pse && (reinterpret_cast<uintptr_t>(workspace) & 7u)) {
-    fa_set_error("workspace must be 8-byte aligned (TND with real_shift)");
+  if (plan->ws_bytes > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15u)) {
+    fa_set_error("workspace must be 16-byte aligned");
     return FA_ERR_WORKSPACE;
   }
   if (p.num_wg == 0) return FA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.has_mask && plan->kind != fa::KERNEL_GENERIC) {  // the generic kernel reads the mask everywhere
+    p.mask_cls = static_cast<uint8_t*>(workspace) + plan->ws_cls_off;
+    const int64_t per_slice = (int64_t)p.cls_tiles * p.cls_kblocks;
+    const int64_t blocks = (int64_t)p.cls_slices * per_slice;
+    if (blocks >= ((int64_t)1 << 31)) {
+      fa_set_error("mask too large to classify");
+      return FA_ERR_RUNTIME;
+    }
+    const int rows = p.varlen ? p.m_rows : p.sq, cols = p.varlen ? p.m_cols : p.skv;
+    const int outside = p.varlen;
+    if (blocks > 0) {
+      void* cargs[] = {(void*)&p.mask, (void*)&p.m_sb, (void*)&p.m_sh, (void*)&p.m_sq, (void*)&p.m_sk, (void*)&p.cls_nh,
+                       (void*)&rows, (void*)&cols, (void*)&p.cls_tiles, (void*)&p.cls_kblocks, (void*)&outside,
+                       (void*)&p.mask_cls};
+      hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::mask_classify), dim3((unsigned)blocks),
+                                     dim3(256), cargs, 0, s);
+      if (e != hipSuccess) return runtime_fail("mask classification launch", e);
+    }
+  }
   if (p.varlen) {
     p.tile_prefix = static_cast<int32_t*>(workspace);
     void* args[] = {(void*)&p.cu_q, (void*)&p.tq, (void*)&p.nbatch, (void*)&plan->bm, (void*)&p.tile_prefix};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::varlen_tile_prefix), dim3(1), dim3(256), args, 0, s);
     if (e != hipSuccess) return runtime_fail("tile prefix launch", e);
     if (p.has_pse) {
-      const uintptr_t o = ((uintptr_t)(p.nbatch + 1) * sizeof(int32_t) + 7) / 8 * 8;
-      p.pse_off = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + o);
+      p.pse_off = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + plan->ws_pse_off);
       void* pargs[] = {(void*)&p.cu_q, (void*)&p.cu_kv, (void*)&p.tq, (void*)&p.tkv, (void*)&p.nbatch, (void*)&p.nq,
                        (void*)&p.pse_off};
       e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::varlen_pse_prefix), dim3(1), dim3(256), pargs, 0, s);

@@ -111,6 +111,7 @@ struct LoopCtx {
   const uint8_t* mrow;              // this lane's mask row (edge blocks)
   const T* pse;                     // additive bias, or null
   int64_t prow;                     // element index of this lane's pse row at key 0
+  const uint8_t* cls_row;           // this tile's mask block classes (null: outside a TND mask)
   int skv, row, i0, last_row;
   int lane, wave, l32, hh;
   bool row_ok;
@@ -163,16 +164,19 @@ __device__ __forceinline__ void stage_block(char* __restrict__ st, int jb, const
   }
 }
 
-// Whether the block at jb needs per-element tests (window edge, sequence end)
-// and whether it reads the mask.
+// Whether the block at jb needs per-element tests (window edge, sequence end,
+// a mixed mask block, pse), whether it reads the mask, and whether the mask
+// excludes all of it (then it is skipped).
 struct BlockKind {
-  bool partial, read_mask;
+  bool partial, read_mask, skip;
 };
-__device__ __forceinline__ BlockKind block_kind(const Params& p, int jb, int skv, int first_row, int last_row) {
-  const bool tail = jb + kMfmaBN > skv;
-  const bool edge = p.band && !(jb >= last_row - p.pre && jb + kMfmaBN - 1 <= first_row + p.next);
-  const bool rm = p.has_mask && (p.mask_everywhere || edge || tail);
-  return {tail || edge || rm || p.has_pse, rm};
+template <typename T>
+__device__ __forceinline__ BlockKind block_kind(const Params& p, int jb, const LoopCtx<T>& x) {
+  const bool tail = jb + kMfmaBN > x.skv;
+  const bool edge = p.band && !(jb >= x.last_row - p.pre && jb + kMfmaBN - 1 <= x.i0 + p.next);
+  const int cls = mask_class(p, x.cls_row, jb);
+  const bool rm = cls == CLS_MIXED;
+  return {tail || edge || rm || p.has_pse, rm, cls == CLS_EXCLUDED};
 }
 
 // Mask bytes of this lane's row for keys jb + 32t + 8a + 4hh + 0..3, word 4t + a
@@ -264,9 +268,9 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
                                   : cur + C::KR_OFF + (r * C::KRU + k_swz(r, 2 * (ks - D / 16) + hh)) * 16;
     return *reinterpret_cast<const V8*>(src);
   };
-  const BlockKind bk = block_kind(p, jb, x.skv, x.i0, x.last_row);
+  const BlockKind bk = block_kind(p, jb, x);
   f32x16 sacc[2];
-  {
+  if (!bk.skip) {  // a block the mask excludes as a whole only keeps the pipeline going
     const V8 a0 = kfrag(0, 0), a1 = kfrag(0, 1);
     if (bk.partial) {
       f32x16 bias[2];
@@ -295,11 +299,12 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
 
   if (more) {
     stage_block<T, D, DR>(nxt, jb + BN, x);
-    if (block_kind(p, jb + BN, x.skv, x.i0, x.last_row).read_mask) fetch_mask(mw, p, jb + BN, x);
+    if (block_kind(p, jb + BN, x).read_mask) fetch_mask(mw, p, jb + BN, x);
     if constexpr (DR == 0) {
       if (p.has_pse) fetch_pse(pw, p, jb + BN, x);
     }
   }
+  if (bk.skip) return;
 
 #pragma unroll
   for (int ks = 1; ks < C::NKS; ++ks) {
@@ -434,6 +439,7 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
     else
       x.mrow = p.mask + tl.b * p.m_sb + tl.h * p.m_sh + (int64_t)(row_ok ? row : 0) * p.m_sq;
   }
+  x.cls_row = mask_class_row(p, tl, i0);
   x.pse = static_cast<const T*>(p.pse);
   x.prow = p.has_pse && row_ok ? pse_row_index(p, tl, row) : 0;
   x.skv = tl.skv;
@@ -452,7 +458,7 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   for (int w = 0; w < 8; ++w) pw[w] = make_uint2(0, 0);
   if (nblocks > 0) {
     stage_block<T, D, DR>(smem, jb0, x);
-    if (block_kind(p, jb0, x.skv, x.i0, x.last_row).read_mask) fetch_mask(mw, p, jb0, x);
+    if (block_kind(p, jb0, x).read_mask) fetch_mask(mw, p, jb0, x);
     if constexpr (DR == 0) {
       if (p.has_pse) fetch_pse(pw, p, jb0, x);
     }

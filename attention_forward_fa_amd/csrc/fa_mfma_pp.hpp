@@ -67,6 +67,7 @@ struct PpCtx {
   const T* krbase;
   int64_t krow_b, vrow_b, krrow_b;
   const uint8_t* mrow;  // this lane's mask row (blocks that read the mask)
+  const uint8_t* cls_row;  // this group's mask block classes (null: outside a TND mask)
   int skv, row, g_first, g_last;
   int lane, wave, l32, hh;
   bool row_ok;
@@ -243,15 +244,15 @@ __device__ __forceinline__ uint32_t pp_mask_word(const Params& p, const PpCtx<T>
 }
 
 // Softmax step of the block at jb (scores in st.sacc) -> st.pk.  Blocks that
-// cross the window edge or the sequence end (or read the mask) first set
-// their excluded scores to -inf.
+// cross the window edge or the sequence end, or whose mask block is mixed,
+// first set their excluded scores to -inf.
 template <typename T, int D, int DR>
 __device__ __forceinline__ void pp_softmax(const Params& p, const PpCtx<T>& x, int jb, PpState<T, D, DR>& st) {
   using C = PpCfg<T, D, DR>;
   constexpr int BN = C::BN;
   const bool tail = jb + BN > x.skv;
   const bool edge = p.band && !(jb >= x.g_last - p.pre && jb + BN - 1 <= x.g_first + p.next);
-  const bool rmask = p.has_mask && (p.mask_everywhere || edge || tail);
+  const bool rmask = mask_class(p, x.cls_row, jb) == CLS_MIXED;
   if (tail || edge || rmask) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -388,9 +389,10 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
   int glo, ghi;
   key_range(p, g_first, g_last, tl.skv, &glo, &ghi);
   const bool g_rows = g_last >= g_first && ghi >= glo;
-  auto active = [&](int k) {
+  const uint8_t* cls_row = mask_class_row(p, tl, g_first);
+  auto active = [&](int k) {  // and not excluded by the mask as a whole
     const int jb = jb0 + k * BN;
-    return g_rows && k < nblocks && jb <= ghi && jb + BN - 1 >= glo;
+    return g_rows && k < nblocks && jb <= ghi && jb + BN - 1 >= glo && mask_class(p, cls_row, jb) != CLS_EXCLUDED;
   };
 
   // ---- running state, log2 domain: t = s * c, c = scale * log2(e)
@@ -421,6 +423,7 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
     else
       x.mrow = p.mask + tl.b * p.m_sb + tl.h * p.m_sh + (int64_t)(row_ok ? row : 0) * p.m_sq;
   }
+  x.cls_row = cls_row;
   x.skv = tl.skv;
   x.row = row;
   x.g_first = g_first;

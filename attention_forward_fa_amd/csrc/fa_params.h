@@ -13,6 +13,14 @@ enum KernelKind : int32_t {
   KERNEL_MFMA_PP = 2,  // as KERNEL_MFMA with 8 waves in two anti-phase groups (BM = 256)
 };
 
+// Mask block classes (written by a pre-pass over the mask): a block of
+// kClsRows query rows x kClsKeys keys whose positions are all kept, all
+// excluded, or mixed.  Only mixed blocks read the mask; excluded ones are
+// skipped.
+constexpr int kClsRows = 128;
+constexpr int kClsKeys = 64;
+enum MaskClass : uint8_t { CLS_KEPT = 0, CLS_EXCLUDED = 1, CLS_MIXED = 2 };
+
 // Tile of the MFMA kernel: 4 wavefronts x 32 query rows, 64 keys per step.
 constexpr int kMfmaBM = 128;
 constexpr int kMfmaBN = 64;
@@ -42,6 +50,7 @@ struct Params {
   int32_t* tile_prefix;  // TND only: workspace, [nbatch + 1]
   const void* pse;       // may be null: additive position bias, q's element type
   int64_t* pse_off;      // TND with pse: workspace, [nbatch + 1] element offset of each sequence's block
+  uint8_t* mask_cls;     // with a mask: workspace, class of every (mask slice, 128-row tile, 64-key block)
 
   // element strides: batch, row (sequence position / token), head
   int64_t q_sb, q_ss, q_sh;
@@ -55,6 +64,8 @@ struct Params {
   int32_t m_rows, m_cols;                // TND: extent of the 2-D mask
   int64_t ps_sb, ps_sh, ps_sq;           // dense pse: batch (0 when broadcast), head, row strides
   int64_t pse_len;                       // elements in the pse tensor; every read is bounded by it
+  int32_t cls_nh, cls_tiles, cls_kblocks;  // mask classes: heads of the mask (1 or N), row tiles, key blocks
+  int32_t cls_slices;                      // mask classes: (mask batch, mask head) slices; 1 for TND
 
   int32_t nbatch;   // B (dense) or number of sequences (TND)
   int32_t nq, nkv, group;
@@ -67,7 +78,6 @@ struct Params {
   int32_t pre, next; // window bounds (next already min(next,0) under causal), clamped
   int32_t band;      // window active (mask given or causal)
   int32_t has_mask, has_sink, varlen;
-  int32_t mask_everywhere;  // read the mask in every block (window cuts nothing)
   int32_t mask_vec4;        // dense mask with contiguous, 4-byte aligned rows: read 4 keys at once
   int32_t has_pse;
   int32_t pse_vec4;         // dense pse whose 4-key groups are 8-byte aligned: read 4 keys at once

@@ -134,12 +134,12 @@ extern "C" int32_t fa_plan_describe(const fa_plan* plan, char* buf, size_t len) 
   const fa::Params& p = plan->p;
   const int n = snprintf(buf, len,
                          "kernel=%s dtype=%s d=%d dr=%d dv=%d bm=%d bn=%d grid=%d block=%d ws=%llu "
-                         "varlen=%d band=%d pre=%d next=%d mask=%d mask_everywhere=%d sink=%d "
+                         "varlen=%d band=%d pre=%d next=%d mask=%d sink=%d "
                          "nq=%d nkv=%d tiles_per_head=%d reverse=%d pse=%d",
                          plan->kind == fa::KERNEL_MFMA_PP ? "mfma_pp" : (plan->kind == fa::KERNEL_MFMA ? "mfma" : "generic"),
                          dtype_name(plan->dtype), p.d, p.dr,
                          p.dv, plan->bm, plan->bn, p.num_wg, plan->block, (unsigned long long)plan->ws_bytes,
-                         p.varlen, p.band, p.pre, p.next, p.has_mask, p.mask_everywhere, p.has_sink, p.nq, p.nkv,
+                         p.varlen, p.band, p.pre, p.next, p.has_mask, p.has_sink, p.nq, p.nkv,
                          p.tiles_per_head, p.reverse_tiles, p.has_pse);
   return n;
 }
@@ -456,11 +456,7 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   p.next = (int32_t)nxt;
   p.has_mask = atten_mask != nullptr;
   p.has_sink = sink != nullptr;
-  // The window cuts nothing when it spans every (row, key) pair: then a given
-  // mask must be read in every block, not just those crossing the window edge.
-  const int64_t max_rows = q.s, max_keys = k.s;  // per-sequence lengths are at most these
-  const bool window_cuts = band && (pre < max_rows - 1 || nxt < max_keys - 1);
-  p.mask_everywhere = p.has_mask && !window_cuts;
+  const int64_t max_keys = k.s;  // per-sequence lengths are at most this
   p.mask_vec4 = p.has_mask && !p.varlen && p.m_sk == 1 && (reinterpret_cast<uintptr_t>(p.mask) & 3u) == 0 &&
                 p.m_sq % 4 == 0 && p.m_sb % 4 == 0 && p.m_sh % 4 == 0;
   p.reverse_tiles = band && nxt < max_keys - 1;
@@ -469,17 +465,49 @@ extern "C" fa_status fa_fwd_get_workspace_size(
 
   const int64_t bm = pl->bm;
   int64_t tiles, wg;
+  // Workspace: [tile prefix, int32, TND] [pse block offsets, int64, TND with
+  // pse] [mask block classes, u8, with a mask], each part 16-byte aligned.
+  uint64_t ws = 0;
+  pl->ws_pse_off = pl->ws_cls_off = 0;
   if (p.varlen) {
     tiles = cdiv(q.s, bm) + nbatch;
     wg = q.s > 0 ? tiles * q.n : 0;
-    // tile prefix (int32), then with pse each sequence's offset into it (int64, 8-aligned)
-    pl->ws_bytes = (uint64_t)(nbatch + 1) * sizeof(int32_t);
-    if (p.has_pse) pl->ws_bytes = (pl->ws_bytes + 7) / 8 * 8 + (uint64_t)(nbatch + 1) * sizeof(int64_t);
+    ws = (uint64_t)(nbatch + 1) * sizeof(int32_t);
+    if (p.has_pse) {
+      pl->ws_pse_off = (ws + 15) / 16 * 16;
+      ws = pl->ws_pse_off + (uint64_t)(nbatch + 1) * sizeof(int64_t);
+    }
   } else {
     tiles = cdiv(q.s, bm);
     wg = tiles * q.b * q.n;
-    pl->ws_bytes = 0;
   }
+  p.mask_cls = nullptr;
+  p.cls_nh = p.cls_tiles = p.cls_kblocks = p.cls_slices = 0;
+  if (p.has_mask) {
+    // dense: one class table per (mask batch, mask head) slice over [Sq, Skv];
+    // TND: one table over the 2-D mask [m_rows, m_cols]
+    const fa_tensor* m = atten_mask;
+    int64_t nslices = 1, rows = q.s, cols = k.s;
+    if (p.varlen) {
+      rows = m->shape[0];
+      cols = m->shape[1];
+    } else if (m->ndim == 4) {
+      nslices = m->shape[0] * m->shape[1];
+      p.cls_nh = (int32_t)m->shape[1];
+    }
+    if (p.cls_nh == 0) p.cls_nh = 1;
+    if (nslices >= ((int64_t)1 << 31)) {
+      delete pl;
+      return fail(FA_ERR_UNSUPPORTED, "mask with %lld slices too large", (long long)nslices);
+    }
+    p.cls_slices = (int32_t)nslices;
+    p.cls_tiles = (int32_t)cdiv(rows, fa::kClsRows);
+    p.cls_kblocks = (int32_t)cdiv(cols, fa::kClsKeys);
+    pl->ws_cls_off = (ws + 15) / 16 * 16;
+    // padded to 16 bytes: the kernels read the table a dword at a time
+    ws = pl->ws_cls_off + ((uint64_t)nslices * p.cls_tiles * p.cls_kblocks + 15) / 16 * 16;
+  }
+  pl->ws_bytes = ws;
   if (wg >= ((int64_t)1 << 31)) {
     delete pl;
     return fail(FA_ERR_UNSUPPORTED, "grid of %lld workgroups too large", (long long)wg);

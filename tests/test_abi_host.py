@@ -291,14 +291,34 @@ def test_band_ignored_without_mask_or_causal():
     _lib.fa_plan_destroy(pl)
 
 
-def test_mask_everywhere_only_when_window_cuts_nothing():
+def test_mask_class_table_in_workspace():
+    """With a mask the workspace holds one class byte per (mask slice, 128-row
+    tile, 64-key block), padded to 16 bytes; TND puts it after the tile prefix."""
     q, k, v, o = c2()
-    m = desc([4096, 4096], U8)
-    st, _, pl = plan(q, k, v, o, mask=m)
-    assert "mask_everywhere=1" in describe(pl)
+    cases = [([4096, 4096], 32 * 64), ([2, 1, 4096, 4096], 2 * 32 * 64), ([1, 24, 4096, 4096], 24 * 32 * 64),
+             ([1, 1, 4096, 4096], 32 * 64)]
+    for shape, want in cases:
+        st, ws, pl = plan(q, k, v, o, mask=desc(shape, U8))
+        assert st == 0, _lib.last_error_message()
+        assert ws == want, (shape, ws)
+        _lib.fa_plan_destroy(pl)
+    # an odd key count: ceil(4000 / 64) = 63 blocks, ceil(4000 / 128) = 32 tiles
+    s = [1, 4000, 2, 128]
+    qq = desc(s)
+    st, ws, pl = plan(qq, qq, qq, qq, mask=desc([4000, 4000], U8))
+    assert st == 0 and ws == (32 * 63 + 15) // 16 * 16, ws
     _lib.fa_plan_destroy(pl)
-    st, _, pl = plan(q, k, v, o, mask=m, nxt=0)
-    assert "mask_everywhere=0" in describe(pl)
+    # TND: tile prefix (6 int32 -> 32 bytes), then the 2-D mask's table (8 x 11 -> 96)
+    T, N = 1000, 4
+    qt = desc([T, N, 128])
+    cu = desc([6], I32)
+    st, ws, pl = plan(qt, qt, qt, qt, cuq=cu, cuk=cu, layout=b"TND", mask=desc([1000, 700], U8))
+    assert st == 0, _lib.last_error_message()
+    assert ws == 32 + 96, ws
+    _lib.fa_plan_destroy(pl)
+    # no mask: no table
+    st, ws, pl = plan(q, k, v, o)
+    assert st == 0 and ws == 0
     _lib.fa_plan_destroy(pl)
 
 
@@ -433,7 +453,7 @@ def test_pse_tnd_workspace():
     cu = desc([6], I32)
     st, ws, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND", pse=desc([12345]))
     assert st == 0, _lib.last_error_message()
-    assert ws == 24 + 8 * 6  # tile prefix (6 int32, padded to 8 bytes) + 6 int64 offsets
+    assert ws == 32 + 8 * 6  # tile prefix (6 int32, padded to 16 bytes) + 6 int64 offsets
     _lib.fa_plan_destroy(pl)
     st, _, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND", pse=desc([10, 10]))
     assert st == 561103 and pl is None

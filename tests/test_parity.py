@@ -84,7 +84,78 @@ SMALL = {
     "pse_tnd": lambda: synth.varlen_case("x", [100, 0, 37, 140], 2, 128, "bf16", 75, causal=True, pse=True),
     "pse_tnd_sink_fp16": lambda: synth.varlen_case("x", [64, 65, 3], 3, 64, "fp16", 76, sink=True, pse=True),
     "pse_unaligned_rows": lambda: synth.dense_case("x", "BNSD", 1, 2, 130, 128, "bf16", 77, skv=131, pse="full"),
+    # general masks: blocks the mask keeps or excludes as a whole, and masks at odds with the window
+    "mask_blocks_aligned": lambda: _block_mask_case(80, 128, 64, (2, 1)),
+    "mask_blocks_unaligned": lambda: _block_mask_case(81, 96, 80, (1, 2)),
+    "mask_blocks_fp16_sink": lambda: _block_mask_case(82, 128, 64, (1, 1), dtype="fp16", sink=True),
+    "mask_blocks_pse": lambda: _block_mask_case(83, 128, 64, (2, 2), pse=True),
+    "mask_blocks_rope_d64": lambda: _block_mask_case(84, 256, 128, (1, 1), d=64, drope=64),
+    "mask_documents": lambda: _document_mask_case(85),
+    "mask_inside_band": lambda: _mask_inside_band_case(86),
+    "mask_outside_band": lambda: _mask_outside_band_case(87),
+    "tnd_mask_blocks": lambda: _tnd_block_mask_case(88),
 }
+
+
+def _block_mask_case(seed, rb, cb, bn, *, dtype="bf16", d=128, drope=0, sink=False, pse=False):
+    """Mask of rb x cb blocks, each excluded (60%), kept (30%) or random (10%),
+    plus one fully excluded row; 700 rows and 650 keys."""
+    c = synth.dense_case("x", "BNSD", 2, 2, 700, d, dtype, seed, skv=650, drope=drope, sink=sink,
+                         pse="full" if pse else None)
+    g = synth.generator(seed + 1000)
+    nr, nc = -(-700 // rb), -(-650 // cb)
+    kind = torch.rand(bn[0], bn[1], nr, nc, generator=g)
+    blk = (kind < 0.6).repeat_interleave(rb, 2).repeat_interleave(cb, 3)[..., :700, :650]
+    rnd = (kind >= 0.9).repeat_interleave(rb, 2).repeat_interleave(cb, 3)[..., :700, :650]
+    noise = torch.rand(bn[0], bn[1], 700, 650, generator=g) < 0.5
+    m = blk | (rnd & noise)
+    m[..., 300, :] = True
+    c.atten_mask = m.to(torch.uint8)
+    return c
+
+
+def _document_mask_case(seed):
+    """Block-diagonal mask of documents whose boundaries differ per batch."""
+    c = synth.dense_case("x", "BSND", 2, 3, 900, 128, "bf16", seed)
+    m = torch.ones(2, 1, 900, 900, dtype=torch.bool)
+    for b, cuts in enumerate(([0, 130, 400, 401, 900], [0, 256, 512, 700, 900])):
+        for a, e in zip(cuts[:-1], cuts[1:]):
+            m[b, 0, a:e, a:e] = False
+    c.atten_mask = m
+    return c
+
+
+def _mask_inside_band_case(seed):
+    """Window of 300 back and 100 ahead; the mask also drops whole blocks and
+    a stripe inside it."""
+    c = synth.dense_case("x", "BNSD", 1, 2, 800, 128, "bf16", seed)
+    i = torch.arange(800).view(-1, 1)
+    j = torch.arange(800).view(1, -1)
+    band_out = ((j - i) > 100) | ((i - j) > 300)
+    holes = ((i // 128) % 2 == 0) & ((j // 64) % 3 == 1)
+    stripe = (j % 97) == 5
+    c.atten_mask = (band_out | holes | stripe).to(torch.uint8)
+    c.pre_tokens, c.next_tokens = 300, 100
+    return c
+
+
+def _mask_outside_band_case(seed):
+    """The mask keeps positions the window excludes (the window still excludes
+    them) and excludes blocks inside it."""
+    c = synth.dense_case("x", "BNSD", 1, 2, 640, 128, "bf16", seed)
+    i = torch.arange(640).view(-1, 1)
+    j = torch.arange(640).view(1, -1)
+    c.atten_mask = (((i // 128) + (j // 64)) % 4 == 0).to(torch.uint8)
+    c.pre_tokens, c.next_tokens = 200, 0
+    return c
+
+
+def _tnd_block_mask_case(seed):
+    c = synth.varlen_case("x", [300, 0, 17, 260], 2, 128, "bf16", seed)
+    i = torch.arange(320).view(-1, 1)
+    j = torch.arange(320).view(1, -1)
+    c.atten_mask = ((((i // 128) + (j // 64)) % 3 == 0) | (j > i + 50)).to(torch.uint8)
+    return c
 
 
 def _pse_band_mask_case(seed):
