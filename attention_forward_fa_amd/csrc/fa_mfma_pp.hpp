@@ -18,12 +18,14 @@
 // then they swap.  The M phase runs at raised wave priority, and its LDS
 // operand reads are issued four MFMAs ahead of their use.
 //
-// K and V: NSLOT slots, block b in slot b % NSLOT.  All 512 threads load
-// block b + NSLOT - 1 at the start of step b (phase 2b); a block is read for
-// the last time in phase 2b + 1, so its slot is free by then.  Every step
-// issues the same loads (past the last block they read zeros into a free
-// slot), and the end of each odd phase waits for all but the newest
-// NSLOT - 3 blocks, so block b + 2 is in LDS before phase 2b + 2.
+// K and V: NSLOT slots, block b in slot b % NSLOT.  In step b each group
+// loads its share of block b + NSLOT - 1 right after the last matrix
+// instruction of its M phase (the loads go out while those drain, and no
+// softmax phase carries them); block b - 1, whose slot they fill, was read
+// for the last time in step b - 1.  Every step issues the same loads (past
+// the last block they read zeros into a free slot), and the end of each odd
+// phase waits for all but the newest NSLOT - 3 blocks, so block b + 2 is in
+// LDS before phase 2b + 2.
 //
 // Masking (window edge, sequence end, explicit mask) is applied to the
 // scores in the softmax step of the blocks that need it.
@@ -147,10 +149,12 @@ constexpr int kPpAhead = 4;
 // The M phase as one stream of MFMAs: the score MFMAs of the block in kslot
 // (when do_s), then the P V MFMAs of the block in vslot (when do_pv), with
 // every LDS operand read issued kPpAhead MFMAs ahead of its use (the
-// sched_group_barrier sequence keeps the compiler from pulling them back).
+// sched_group_barrier sequence keeps the compiler from pulling them back),
+// then this wave's loads of the block at jfill into slot fill.
 template <typename T, int D, int DR>
-__device__ __forceinline__ void pp_mphase(const char* __restrict__ kslot, const char* __restrict__ vslot, bool do_s,
-                                          bool do_pv, const PpCtx<T>& x,
+__device__ __forceinline__ void pp_mphase(const char* __restrict__ kslot, const char* __restrict__ vslot,
+                                          char* __restrict__ fill, int jfill, bool do_s, bool do_pv,
+                                          const PpCtx<T>& x,
                                           const typename Vec8<T>::type (&qf)[PpCfg<T, D, DR>::NKS],
                                           const typename Vec8<T>::type (&pk)[2][2], f32x16 (&s)[2],
                                           f32x16 (&oacc)[PpCfg<T, D, DR>::NDT]) {
@@ -195,6 +199,7 @@ __device__ __forceinline__ void pp_mphase(const char* __restrict__ kslot, const 
         oacc[q % C::NDT] = mfma32<T>(a[j], pk[ts >> 1][ts & 1], oacc[q % C::NDT]);
       }
     }
+    pp_stage<T, D, DR>(fill, jfill, x);
     // keep the reads kPpAhead MFMAs ahead (the scheduler would pull them back)
     __builtin_amdgcn_sched_group_barrier(0x100, kPpAhead, 0);
 #pragma unroll
@@ -206,7 +211,12 @@ __device__ __forceinline__ void pp_mphase(const char* __restrict__ kslot, const 
       else if (n < NS + NP)
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-  } else if (do_s) {
+    // the loads go out after the last MFMA
+    __builtin_amdgcn_sched_group_barrier(0x010, C::LPB, 0);
+    return;
+  }
+  pp_stage<T, D, DR>(fill, jfill, x);
+  if (do_s) {
     V8 a[NS];
 #pragma unroll
     for (int i = 0; i < NS + kPpAhead; ++i) {
@@ -307,7 +317,8 @@ __device__ __forceinline__ void pp_softmax(const Params& p, const PpCtx<T>& x, i
 }
 
 // One step (phases 2k and 2k + 1).  Reads slot cur (block k) and nxt (block
-// k + 1), fills slot fill with block k + NSLOT - 1.  The three pointers are
+// k + 1); each group's M phase fills its share of slot fill with block
+// k + NSLOT - 1.  The three pointers are
 // restrict-qualified, so the compiler knows the operand reads do not depend
 // on the loads in flight.
 template <typename T, int D, int DR>
@@ -316,11 +327,11 @@ __device__ __forceinline__ void pp_step(char* __restrict__ fill, const char* __r
                                         int grp, const Params& p, const PpCtx<T>& x, PpState<T, D, DR>& st) {
   using C = PpCfg<T, D, DR>;
   constexpr int BN = C::BN;
-  pp_stage<T, D, DR>(fill, jb0 + (k + C::NSLOT - 1) * BN, x);
+  const int jfill = jb0 + (k + C::NSLOT - 1) * BN;
   // phase 2k: group 0 = M phase of step k, group 1 = softmax of block k
   if (grp == 0) {
     __builtin_amdgcn_s_setprio(1);
-    pp_mphase<T, D, DR>(nxt, cur, act_k1, act_k, x, st.qf, st.pk, st.sacc, st.oacc);
+    pp_mphase<T, D, DR>(nxt, cur, fill, jfill, act_k1, act_k, x, st.qf, st.pk, st.sacc, st.oacc);
     __builtin_amdgcn_s_setprio(0);
   } else {
     if (k == 0 && act_k) pp_scores<T, D, DR>(cur, x, st.qf, st.sacc);
@@ -332,7 +343,7 @@ __device__ __forceinline__ void pp_step(char* __restrict__ fill, const char* __r
     if (act_k1) pp_softmax<T, D, DR>(p, x, jb0 + (k + 1) * BN, st);
   } else {
     __builtin_amdgcn_s_setprio(1);
-    pp_mphase<T, D, DR>(nxt, cur, act_k1, act_k, x, st.qf, st.pk, st.sacc, st.oacc);
+    pp_mphase<T, D, DR>(nxt, cur, fill, jfill, act_k1, act_k, x, st.qf, st.pk, st.sacc, st.oacc);
     __builtin_amdgcn_s_setprio(0);
   }
 }
