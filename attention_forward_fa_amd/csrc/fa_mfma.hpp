@@ -111,6 +111,7 @@ struct LoopCtx {
   const uint8_t* mrow;              // this lane's mask row (edge blocks)
   const T* pse;                     // additive bias, or null
   int64_t prow;                     // element index of this lane's pse row at key 0
+  int64_t ptile;                    // element index of the tile's first pse row at key 0
   const uint8_t* cls_row;           // this tile's mask block classes (null: outside a TND mask)
   int skv, row, i0, last_row;
   int lane, wave, l32, hh;
@@ -168,7 +169,7 @@ __device__ __forceinline__ void stage_block(char* __restrict__ st, int jb, const
 // a mixed mask block, pse), whether it reads the mask, and whether the mask
 // excludes all of it (then it is skipped).
 struct BlockKind {
-  bool partial, read_mask, skip;
+  bool partial, tests, read_mask, skip;
 };
 template <typename T>
 __device__ __forceinline__ BlockKind block_kind(const Params& p, int jb, const LoopCtx<T>& x) {
@@ -176,7 +177,8 @@ __device__ __forceinline__ BlockKind block_kind(const Params& p, int jb, const L
   const bool edge = p.band && !(jb >= x.last_row - p.pre && jb + kMfmaBN - 1 <= x.i0 + p.next);
   const int cls = mask_class(p, x.cls_row, jb);
   const bool rm = cls == CLS_MIXED;
-  return {tail || edge || rm || p.has_pse, rm, cls == CLS_EXCLUDED};
+  const bool tests = tail || edge || rm;
+  return {tests || p.has_pse, tests, rm, cls == CLS_EXCLUDED};
 }
 
 // Mask bytes of this lane's row for keys jb + 32t + 8a + 4hh + 0..3, word 4t + a
@@ -236,6 +238,38 @@ __device__ __forceinline__ float pse_elem(const uint2& w, int b) {
   return to_f32(__builtin_bit_cast(T, bits));
 }
 
+// pse through LDS (dense pse with 16-byte aligned rows): the tile of the
+// workgroup's 128 rows x 64 keys is loaded straight into LDS with coalesced
+// 16-byte loads, row-major with the 16-byte units of row r XOR-swizzled by
+// (r / 2) % 8, so that the per-lane reads below (32 rows, one unit each) hit
+// every bank twice at most.
+constexpr int kPseTileBytes = kMfmaBM * kMfmaBN * 2;
+
+template <typename T>
+__device__ __forceinline__ void pse_stage(char* __restrict__ tile, const Params& p, int jb, const LoopCtx<T>& x) {
+  const int64_t base = x.ptile + jb;  // inside the tensor: row i0 < Sq, key jb < Skv
+  const T* src = x.pse + base;
+  const int64_t nbytes = (p.pse_len - base) * (int64_t)sizeof(T);
+#pragma unroll
+  for (int n = 0; n < kPseTileBytes / 16 / kMfmaThreads; ++n) {
+    const int unit = 64 * (4 * n + x.wave) + x.lane;  // physical unit
+    const int r = unit >> 3, c = (unit & 7) ^ ((r >> 1) & 7);
+    dma16(src, nbytes, (lds_void*)(tile + 1024 * (4 * n + x.wave)),
+          (uint32_t)(((int64_t)r * p.ps_sq + 8 * c) * (int64_t)sizeof(T)));
+  }
+}
+
+// This lane's pse words from the LDS tile, in fetch_pse's layout.
+template <typename T>
+__device__ __forceinline__ void pse_read(uint2 (&pw)[8], const char* tile, const LoopCtx<T>& x) {
+  const int r = 32 * x.wave + x.l32;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int c = w ^ ((r >> 1) & 7);  // logical unit w = keys 8w .. 8w + 7
+    pw[w] = *reinterpret_cast<const uint2*>(tile + (r * 8 + c) * 16 + 8 * x.hh);
+  }
+}
+
 // One key block: prefetch the next block (and its mask words) into `nxt`,
 // then the scores from `cur`, the softmax step and the output update.  The
 // two stage pointers are restrict-qualified so the compiler knows the LDS
@@ -246,9 +280,10 @@ __device__ __forceinline__ float pse_elem(const uint2& w, int b) {
 // Excluded positions are applied before the score product: the accumulators
 // start at 0 for kept and -inf for excluded elements, and the MFMA adds K Q^T
 // to them (-inf + finite = -inf).  Nothing branches after the scores.
-template <typename T, int D, int DR>
-__device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __restrict__ nxt, int jb, bool more,
-                                          const Params& p, const LoopCtx<T>& x,
+template <typename T, int D, int DR, bool PL>
+__device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __restrict__ nxt,
+                                          char* __restrict__ ptile, int jb, bool more, const Params& p,
+                                          const LoopCtx<T>& x,
                                           const typename Vec8<T>::type (&qf)[MfmaCfg<T, D, DR>::NKS],
                                           f32x16 (&oacc)[MfmaCfg<T, D, DR>::NDT], float& m_ref, float& m_max,
                                           float& lsum, uint32_t (&mw)[8], uint2 (&pw)[8]) {
@@ -272,7 +307,15 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
   f32x16 sacc[2];
   if (!bk.skip) {  // a block the mask excludes as a whole only keeps the pipeline going
     const V8 a0 = kfrag(0, 0), a1 = kfrag(0, 1);
-    if (bk.partial) {
+    if (DR == 0 && p.has_pse && !bk.tests) {  // pse only: no exclusion tests
+      f32x16 bias[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) bias[t][j] = pse_elem<T>(pw[4 * t + (j >> 2)], j & 3) * p.inv_scale;
+      sacc[0] = mfma32<T>(a0, qf[0], bias[0]);
+      sacc[1] = mfma32<T>(a1, qf[0], bias[1]);
+    } else if (bk.partial) {
       f32x16 bias[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -300,7 +343,13 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
   if (more) {
     stage_block<T, D, DR>(nxt, jb + BN, x);
     if (block_kind(p, jb + BN, x).read_mask) fetch_mask(mw, p, jb + BN, x);
-    if constexpr (DR == 0) {
+    if constexpr (PL) {
+      // every wave has its words of this block's tile (read after the last
+      // barrier, consumed above): the tile can take the next block
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      pse_stage<T>(ptile, p, jb + BN, x);
+    } else if constexpr (DR == 0) {
       if (p.has_pse) fetch_pse(pw, p, jb + BN, x);
     }
   }
@@ -365,12 +414,15 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
   }
 }
 
-template <typename T, int D, int DR>
+// PL: pse staged through LDS (dense pse with 16-byte aligned rows, no rope).
+template <typename T, int D, int DR, bool PL = false>
 __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   using C = MfmaCfg<T, D, DR>;
   using V8 = typename Vec8<T>::type;
   constexpr int BM = C::BM, BN = C::BN;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
+  static_assert(!PL || DR == 0, "pse and rope do not combine");
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES + (PL ? kPseTileBytes : 0)];
+  char* const ptile = smem + 2 * C::STAGE_BYTES;
 
   const Tile tl = map_tile(p, blockIdx.x);
   if (!tl.valid) return;
@@ -442,6 +494,7 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   x.cls_row = mask_class_row(p, tl, i0);
   x.pse = static_cast<const T*>(p.pse);
   x.prow = p.has_pse && row_ok ? pse_row_index(p, tl, row) : 0;
+  x.ptile = PL ? pse_row_index(p, tl, i0) : 0;
   x.skv = tl.skv;
   x.row = row;
   x.i0 = i0;
@@ -459,21 +512,30 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   if (nblocks > 0) {
     stage_block<T, D, DR>(smem, jb0, x);
     if (block_kind(p, jb0, x).read_mask) fetch_mask(mw, p, jb0, x);
-    if constexpr (DR == 0) {
+    if constexpr (PL) {
+      pse_stage<T>(ptile, p, jb0, x);
+    } else if constexpr (DR == 0) {
       if (p.has_pse) fetch_pse(pw, p, jb0, x);
     }
   }
   // Wait here once for the Q fragments, the first block and its mask words.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   __syncthreads();
+  if constexpr (PL) {
+    if (nblocks > 0) pse_read<T>(pw, ptile, x);
+  }
 
   for (int it = 0; it < nblocks; ++it) {
     const int stg = it & 1;
-    key_block<T, D, DR>(smem + stg * C::STAGE_BYTES, smem + (stg ^ 1) * C::STAGE_BYTES, jb0 + it * BN,
-                        it + 1 < nblocks, p, x, qf, oacc, m_ref, m_max, lsum, mw, pw);
+    const bool more = it + 1 < nblocks;
+    key_block<T, D, DR, PL>(smem + stg * C::STAGE_BYTES, smem + (stg ^ 1) * C::STAGE_BYTES, ptile, jb0 + it * BN,
+                            more, p, x, qf, oacc, m_ref, m_max, lsum, mw, pw);
     // this thread's loads of the next block landed; then everyone's, before the swap
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
+    if constexpr (PL) {
+      if (more) pse_read<T>(pw, ptile, x);
+    }
   }
 
   // ---- epilogue: O = O / l, statistics at the true max

@@ -26,7 +26,11 @@ template <typename T>
 static hipError_t launch_mfma_t(const Params& p, hipStream_t s) {
   void* args[] = {const_cast<Params*>(&p)};
   const void* fn = nullptr;
-  if (p.d == 128 && p.dr == 0)
+  if (p.pse_lds && p.d == 128 && p.dr == 0)
+    fn = reinterpret_cast<const void*>(&fa_fwd_mfma<T, 128, 0, true>);
+  else if (p.pse_lds && p.d == 64 && p.dr == 0)
+    fn = reinterpret_cast<const void*>(&fa_fwd_mfma<T, 64, 0, true>);
+  else if (p.d == 128 && p.dr == 0)
     fn = reinterpret_cast<const void*>(&fa_fwd_mfma<T, 128, 0>);
   else if (p.d == 128 && p.dr == 64)
     fn = reinterpret_cast<const void*>(&fa_fwd_mfma<T, 128, 64>);

@@ -81,6 +81,7 @@ struct Params {
   int32_t mask_vec4;        // dense mask with contiguous, 4-byte aligned rows: read 4 keys at once
   int32_t has_pse;
   int32_t pse_vec4;         // dense pse whose 4-key groups are 8-byte aligned: read 4 keys at once
+  int32_t pse_lds;          // dense pse with 16-byte aligned rows: staged through LDS by the matrix-core kernel
   float inv_scale;          // 1 / scale: pse enters the raw score accumulator as pse / scale
 
   int32_t tiles_per_head;   // dense: ceil(sq / BM); TND: ceil(tq / BM) + nbatch (upper bound)

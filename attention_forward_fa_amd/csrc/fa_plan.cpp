@@ -135,12 +135,12 @@ extern "C" int32_t fa_plan_describe(const fa_plan* plan, char* buf, size_t len) 
   const int n = snprintf(buf, len,
                          "kernel=%s dtype=%s d=%d dr=%d dv=%d bm=%d bn=%d grid=%d block=%d ws=%llu "
                          "varlen=%d band=%d pre=%d next=%d mask=%d sink=%d "
-                         "nq=%d nkv=%d tiles_per_head=%d reverse=%d pse=%d",
+                         "nq=%d nkv=%d tiles_per_head=%d reverse=%d pse=%d pse_lds=%d",
                          plan->kind == fa::KERNEL_MFMA_PP ? "mfma_pp" : (plan->kind == fa::KERNEL_MFMA ? "mfma" : "generic"),
                          dtype_name(plan->dtype), p.d, p.dr,
                          p.dv, plan->bm, plan->bn, p.num_wg, plan->block, (unsigned long long)plan->ws_bytes,
                          p.varlen, p.band, p.pre, p.next, p.has_mask, p.has_sink, p.nq, p.nkv,
-                         p.tiles_per_head, p.reverse_tiles, p.has_pse);
+                         p.tiles_per_head, p.reverse_tiles, p.has_pse, p.pse_lds);
   return n;
 }
 
@@ -462,6 +462,8 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   p.reverse_tiles = band && nxt < max_keys - 1;
   p.pse_vec4 = p.has_pse && !p.varlen && (reinterpret_cast<uintptr_t>(p.pse) & 7u) == 0 && p.ps_sq % 4 == 0 &&
                p.ps_sb % 4 == 0 && p.ps_sh % 4 == 0;
+  p.pse_lds = p.has_pse && !p.varlen && dr == 0 && (reinterpret_cast<uintptr_t>(p.pse) & 15u) == 0 &&
+              p.ps_sq % 8 == 0 && p.ps_sb % 8 == 0 && p.ps_sh % 8 == 0 && p.ps_sq < ((int64_t)1 << 24);
 
   const int64_t bm = pl->bm;
   int64_t tiles, wg;

@@ -418,7 +418,15 @@ def test_pse_plan_and_validation():
     st, ws, pl = plan(q, q, q, q, pse=ok, layout=b"BNSD")
     assert st == 0, _lib.last_error_message()
     d = describe(pl)
-    assert "pse=1" in d and "kernel=mfma " in d, d
+    assert "pse=1" in d and "kernel=mfma " in d and "pse_lds=1" in d, d
+    _lib.fa_plan_destroy(pl)
+    # rows that are not a multiple of 8 keys, or a base off 16 bytes: per-lane reads
+    odd = desc([B, N, S, S + 4])
+    st, _, pl = plan(q, desc([B, N, S + 4, D]), desc([B, N, S + 4, D]), q, pse=odd, layout=b"BNSD")
+    assert st == 0 and "pse_lds=0" in describe(pl), describe(pl)
+    _lib.fa_plan_destroy(pl)
+    st, _, pl = plan(q, q, q, q, pse=desc([B, N, S, S], addr=ADDR + 8), layout=b"BNSD")
+    assert st == 0 and "pse_lds=0" in describe(pl), describe(pl)
     _lib.fa_plan_destroy(pl)
     st, _, pl = plan(q, q, q, q, pse=desc([1, N, S, S]), layout=b"BNSD")  # broadcast over batch
     assert st == 0, _lib.last_error_message()

@@ -84,6 +84,13 @@ SMALL = {
     "pse_tnd": lambda: synth.varlen_case("x", [100, 0, 37, 140], 2, 128, "bf16", 75, causal=True, pse=True),
     "pse_tnd_sink_fp16": lambda: synth.varlen_case("x", [64, 65, 3], 3, 64, "fp16", 76, sink=True, pse=True),
     "pse_unaligned_rows": lambda: synth.dense_case("x", "BNSD", 1, 2, 130, 128, "bf16", 77, skv=131, pse="full"),
+    # pse staged through LDS (rows a multiple of 8 keys, 16-byte aligned)
+    "pse_lds_causal_ragged": lambda: synth.dense_case("x", "BNSD", 2, 2, 200, 128, "bf16", 90, skv=264, pse="full",
+                                                      causal=True),
+    "pse_lds_d64_bcast_fp16": lambda: synth.dense_case("x", "BSND", 1, 3, 300, 64, "fp16", 91, skv=256,
+                                                       pse="bcast"),
+    "pse_lds_band_mask_sink": lambda: _pse_lds_mask_case(92),
+    "pse_lds_blocks": lambda: _block_mask_case(93, 128, 64, (1, 1), pse=True, skv=640),
     # general masks: blocks the mask keeps or excludes as a whole, and masks at odds with the window
     "mask_blocks_aligned": lambda: _block_mask_case(80, 128, 64, (2, 1)),
     "mask_blocks_unaligned": lambda: _block_mask_case(81, 96, 80, (1, 2)),
@@ -97,20 +104,29 @@ SMALL = {
 }
 
 
-def _block_mask_case(seed, rb, cb, bn, *, dtype="bf16", d=128, drope=0, sink=False, pse=False):
+def _block_mask_case(seed, rb, cb, bn, *, dtype="bf16", d=128, drope=0, sink=False, pse=False, skv=650):
     """Mask of rb x cb blocks, each excluded (60%), kept (30%) or random (10%),
-    plus one fully excluded row; 700 rows and 650 keys."""
-    c = synth.dense_case("x", "BNSD", 2, 2, 700, d, dtype, seed, skv=650, drope=drope, sink=sink,
+    plus one fully excluded row; 700 rows and skv keys."""
+    c = synth.dense_case("x", "BNSD", 2, 2, 700, d, dtype, seed, skv=skv, drope=drope, sink=sink,
                          pse="full" if pse else None)
     g = synth.generator(seed + 1000)
-    nr, nc = -(-700 // rb), -(-650 // cb)
+    nr, nc = -(-700 // rb), -(-skv // cb)
     kind = torch.rand(bn[0], bn[1], nr, nc, generator=g)
-    blk = (kind < 0.6).repeat_interleave(rb, 2).repeat_interleave(cb, 3)[..., :700, :650]
-    rnd = (kind >= 0.9).repeat_interleave(rb, 2).repeat_interleave(cb, 3)[..., :700, :650]
-    noise = torch.rand(bn[0], bn[1], 700, 650, generator=g) < 0.5
+    blk = (kind < 0.6).repeat_interleave(rb, 2).repeat_interleave(cb, 3)[..., :700, :skv]
+    rnd = (kind >= 0.9).repeat_interleave(rb, 2).repeat_interleave(cb, 3)[..., :700, :skv]
+    noise = torch.rand(bn[0], bn[1], 700, skv, generator=g) < 0.5
     m = blk | (rnd & noise)
     m[..., 300, :] = True
     c.atten_mask = m.to(torch.uint8)
+    return c
+
+
+def _pse_lds_mask_case(seed):
+    c = synth.dense_case("x", "BNSD", 1, 2, 330, 128, "bf16", seed, skv=320, sink=True, pse="full")
+    i = torch.arange(330).view(-1, 1)
+    j = torch.arange(320).view(1, -1)
+    c.atten_mask = (((j - i) > 30) | ((i - j) > 150) | ((j % 61) == 7)).to(torch.uint8)
+    c.pre_tokens, c.next_tokens = 150, 30
     return c
 
 
