@@ -304,6 +304,15 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
     return *reinterpret_cast<const V8*>(src);
   };
   const BlockKind bk = block_kind(p, jb, x);
+  if constexpr (PL) {
+    if (more) {
+      // every wave has its words of this block's pse tile in registers (read
+      // after the last barrier): the tile can take the next block's
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      pse_stage<T>(ptile, p, jb + BN, x);
+    }
+  }
   f32x16 sacc[2];
   if (!bk.skip) {  // a block the mask excludes as a whole only keeps the pipeline going
     const V8 a0 = kfrag(0, 0), a1 = kfrag(0, 1);
@@ -343,13 +352,7 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
   if (more) {
     stage_block<T, D, DR>(nxt, jb + BN, x);
     if (block_kind(p, jb + BN, x).read_mask) fetch_mask(mw, p, jb + BN, x);
-    if constexpr (PL) {
-      // every wave has its words of this block's tile (read after the last
-      // barrier, consumed above): the tile can take the next block
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-      __builtin_amdgcn_s_barrier();
-      pse_stage<T>(ptile, p, jb + BN, x);
-    } else if constexpr (DR == 0) {
+    if constexpr (!PL && DR == 0) {
       if (p.has_pse) fetch_pse(pw, p, jb + BN, x);
     }
   }
