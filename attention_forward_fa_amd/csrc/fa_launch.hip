@@ -74,7 +74,7 @@ __global__ void __launch_bounds__(256) varlen_pse_prefix(const int32_t* __restri
 // read them.  Class: all counted positions kept, all excluded, or mixed.
 __global__ void __launch_bounds__(256) mask_classify(const uint8_t* __restrict__ mask, int64_t m_sb, int64_t m_sh,
                                                      int64_t m_sq, int64_t m_sk, int nh, int rows, int cols,
-                                                     int tiles, int kblocks, int outside_excluded,
+                                                     int tiles, int kblocks, int outside_excluded, int vec,
                                                      uint8_t* __restrict__ cls) {
   const int64_t id = blockIdx.x;
   const int kb = (int)(id % kblocks);
@@ -86,14 +86,26 @@ __global__ void __launch_bounds__(256) mask_classify(const uint8_t* __restrict__
   const int r = t * kClsRows + (threadIdx.x >> 1);
   const int c0 = kb * kClsKeys + 32 * (threadIdx.x & 1);
   bool kept = false, excl = false;
-  for (int c = c0; c < c0 + 32; ++c) {
-    const bool inside = r < rows && c < cols;
-    if (inside) {
-      const bool e = base[(int64_t)r * m_sq + (int64_t)c * m_sk] != 0;
-      kept |= !e;
-      excl |= e;
-    } else if (outside_excluded) {
-      excl = true;
+  if (vec && r < rows && c0 + 32 <= cols) {
+    // 32 contiguous bytes of the row: two 16-byte loads
+    const uint4* src = reinterpret_cast<const uint4*>(base + (int64_t)r * m_sq + c0);
+    const uint4 a = src[0], b = src[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      kept |= ((w[i] - 0x01010101u) & ~w[i] & 0x80808080u) != 0;  // some byte is 0
+      excl |= w[i] != 0;
+    }
+  } else {
+    for (int c = c0; c < c0 + 32; ++c) {
+      const bool inside = r < rows && c < cols;
+      if (inside) {
+        const bool e = base[(int64_t)r * m_sq + (int64_t)c * m_sk] != 0;
+        kept |= !e;
+        excl |= e;
+      } else if (outside_excluded) {
+        excl = true;
+      }
     }
   }
   const int any_kept = __syncthreads_or(kept);
@@ -143,10 +155,13 @@ extern "C" fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_p
     }
     const int rows = p.varlen ? p.m_rows : p.sq, cols = p.varlen ? p.m_cols : p.skv;
     const int outside = p.varlen;
+    // rows of contiguous bytes, 16-byte aligned: vector loads
+    const int vec = p.m_sk == 1 && (reinterpret_cast<uintptr_t>(p.mask) & 15u) == 0 && p.m_sq % 16 == 0 &&
+                    p.m_sb % 16 == 0 && p.m_sh % 16 == 0;
     if (blocks > 0) {
       void* cargs[] = {(void*)&p.mask, (void*)&p.m_sb, (void*)&p.m_sh, (void*)&p.m_sq, (void*)&p.m_sk, (void*)&p.cls_nh,
                        (void*)&rows, (void*)&cols, (void*)&p.cls_tiles, (void*)&p.cls_kblocks, (void*)&outside,
-                       (void*)&p.mask_cls};
+                       (void*)&vec, (void*)&p.mask_cls};
       hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::mask_classify), dim3((unsigned)blocks),
                                      dim3(256), cargs, 0, s);
       if (e != hipSuccess) return runtime_fail("mask classification launch", e);

@@ -9,7 +9,9 @@
 // which follows from the definitions of softmaxMax and softmaxSum in the sink
 // equations of the aclnnFlashAttentionVarLenScoreV5 page.  Chunks with no kept
 // key (m_c = -inf, l_c = 0) weigh 0; a row empty in every chunk gets O = 0,
-// m = -inf, l = 0.  Memory-bound: one wavefront per row, lanes along Dv.
+// m = -inf, l = 0.  Memory-bound: with 16-byte aligned rows a thread merges
+// 8 consecutive output elements (one 16-byte load per part), otherwise one
+// wavefront per row with lanes along Dv.
 #include <hip/hip_runtime.h>
 
 #include "fa_device.hpp"
@@ -58,11 +60,91 @@ __global__ void __launch_bounds__(256) fa_merge_kernel(const MergeParams mp) {
   }
 }
 
+// Row weights of the parts: w_c = e^(m_c - m) l_c (0 for an empty part).
+__device__ __forceinline__ void merge_weights(const MergeParams& mp, int b, int h, int s, float (&w)[kMergeMaxParts],
+                                              float& m, float& l) {
+  float mc[kMergeMaxParts];
+  m = kNegInf;
+  for (int c = 0; c < mp.nparts; ++c) {
+    const int64_t si = b * mp.pst_sb[c] + h * mp.pst_sh[c] + s * mp.pst_ss[c];
+    mc[c] = mp.pm[c][si];
+    w[c] = mp.pl[c][si];
+    m = fmaxf(m, mc[c]);
+  }
+  l = 0.f;
+  for (int c = 0; c < mp.nparts; ++c) {
+    w[c] = mc[c] == kNegInf ? 0.f : expf(mc[c] - m) * w[c];
+    l += w[c];
+  }
+}
+
+// 16-byte path: thread = (row, 8-element chunk); rows of dv / 8 chunks.
+template <typename T>
+__global__ void __launch_bounds__(256) fa_merge_vec_kernel(const MergeParams mp) {
+  const int cpr = mp.dv / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = t / cpr;
+  const int chunk = (int)(t - r * cpr);
+  const int64_t per_b = (int64_t)mp.nheads * mp.nrows;
+  if (r >= per_b * mp.nbatch) return;
+  const int b = (int)(r / per_b);
+  const int h = (int)((r - b * per_b) / mp.nrows);
+  const int s = (int)(r - b * per_b - (int64_t)h * mp.nrows);
+  float w[kMergeMaxParts], m, l;
+  merge_weights(mp, b, h, s, w, m, l);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < mp.nparts; ++c) {
+    const T* oc = static_cast<const T*>(mp.po[c]) + b * mp.po_sb[c] + h * mp.po_sh[c] + s * mp.po_ss[c] + 8 * chunk;
+    const uint4 u = *reinterpret_cast<const uint4*>(oc);
+    const T* e = reinterpret_cast<const T*>(&u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[c], to_f32(e[i]), acc[i]);
+  }
+  T res[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) res[i] = from_f32<T>(acc[i] * inv);
+  T* o = static_cast<T*>(mp.o) + b * mp.o_sb + h * mp.o_sh + s * mp.o_ss + 8 * chunk;
+  *reinterpret_cast<uint4*>(o) = *reinterpret_cast<const uint4*>(res);
+  if (chunk == 0) {
+    const int64_t so = b * mp.st_sb + h * mp.st_sh + s * mp.st_ss;
+    if (mp.m) {
+      reinterpret_cast<float4*>(mp.m + so)[0] = make_float4(m, m, m, m);
+      reinterpret_cast<float4*>(mp.m + so)[1] = make_float4(m, m, m, m);
+    }
+    if (mp.l) {
+      reinterpret_cast<float4*>(mp.l + so)[0] = make_float4(l, l, l, l);
+      reinterpret_cast<float4*>(mp.l + so)[1] = make_float4(l, l, l, l);
+    }
+  }
+}
+
+// Whether every row the merge touches is 16-byte aligned (outputs) and the
+// statistics rows are 16-byte aligned (8 fp32 slots).
+template <typename T>
+static bool merge_vec_ok(const MergeParams& mp) {
+  if (sizeof(T) != 2 || mp.dv % 8 != 0) return false;
+  auto al = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; };
+  auto st = [](int64_t x) { return x % 8 == 0; };
+  for (int c = 0; c < mp.nparts; ++c)
+    if (!al(mp.po[c]) || !st(mp.po_sb[c]) || !st(mp.po_sh[c]) || !st(mp.po_ss[c])) return false;
+  if (!al(mp.o) || !st(mp.o_sb) || !st(mp.o_sh) || !st(mp.o_ss)) return false;
+  const bool stats_ok = (!mp.m || al(mp.m)) && (!mp.l || al(mp.l));
+  return stats_ok && (mp.st_sb % 4 == 0) && (mp.st_sh % 4 == 0) && (mp.st_ss % 4 == 0);
+}
+
 int merge_launch(const MergeParams& mp, int32_t dtype, void* stream) {
   const int64_t rows = (int64_t)mp.nbatch * mp.nheads * mp.nrows;
   if (rows == 0) return 0;
   void* args[] = {const_cast<MergeParams*>(&mp)};
   const void* fn = nullptr;
+  if (dtype == FA_DTYPE_BF16 && merge_vec_ok<__bf16>(mp)) fn = reinterpret_cast<const void*>(&fa_merge_vec_kernel<__bf16>);
+  if (dtype == FA_DTYPE_F16 && merge_vec_ok<_Float16>(mp)) fn = reinterpret_cast<const void*>(&fa_merge_vec_kernel<_Float16>);
+  if (fn) {
+    const int64_t threads = rows * (mp.dv / 8);
+    return (int)hipLaunchKernel(fn, dim3((unsigned)((threads + 255) / 256)), dim3(256), args, 0,
+                                static_cast<hipStream_t>(stream));
+  }
   switch (dtype) {
     case FA_DTYPE_F32: fn = reinterpret_cast<const void*>(&fa_merge_kernel<float>); break;
     case FA_DTYPE_F16: fn = reinterpret_cast<const void*>(&fa_merge_kernel<_Float16>); break;
