@@ -428,6 +428,10 @@ def test_pse_plan_and_validation():
     st, _, pl = plan(q, q, q, q, pse=desc([B, N, S, S], addr=ADDR + 8), layout=b"BNSD")
     assert st == 0 and "pse_lds=0" in describe(pl), describe(pl)
     _lib.fa_plan_destroy(pl)
+    # pse with the rope term is not combined
+    qr = desc([B, N, S, 64])
+    st, _, pl = plan(q, q, q, q, qr=qr, kr=qr, pse=ok, layout=b"BNSD")
+    assert st == 561103 and pl is None and "rope" in _lib.last_error_message()
     st, _, pl = plan(q, q, q, q, pse=desc([1, N, S, S]), layout=b"BNSD")  # broadcast over batch
     assert st == 0, _lib.last_error_message()
     _lib.fa_plan_destroy(pl)
