@@ -101,6 +101,37 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // brought to it once at the end.
 constexpr float kLazy = 8.0f;
 
+// Epilogue through LDS.  Every lane writes its row's output values (the
+// transposed accumulator: columns 32 dt + 8 g4 + 4 hh .. +3 of local row
+// lrow) into an LDS tile of BM rows x DV columns whose 16-byte units are
+// XOR-swizzled by the row (the lanes of one store, 32 rows at one column,
+// then hit distinct banks); after a barrier the workgroup stores whole rows
+// with 16-byte writes, so each row leaves as one contiguous run.  Rows at or
+// past nrows are not written.  Every thread of the workgroup must call it;
+// the LDS must no longer be in use (no loads in flight into it).
+template <typename T, int DV, int NTHREADS>
+__device__ __forceinline__ void o_tile_store(char* __restrict__ lds, const f32x16 (&oacc)[DV / 32], float inv,
+                                             int lrow, int hh, T* __restrict__ obase, int64_t o_ss, int nrows) {
+  constexpr int U = DV / 8;  // 16-byte units per row
+#pragma unroll
+  for (int dt = 0; dt < DV / 32; ++dt) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      T v4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = from_f32<T>(oacc[dt][4 * g4 + e] * inv);
+      const int pu = (4 * dt + g4) ^ (lrow % U);
+      *reinterpret_cast<uint2*>(lds + (lrow * U + pu) * 16 + 8 * hh) = *reinterpret_cast<const uint2*>(v4);
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nrows * U; idx += NTHREADS) {
+    const int r = idx / U, u = idx - r * U;
+    const uint4 v = *reinterpret_cast<const uint4*>(lds + (r * U + (u ^ (r % U))) * 16);
+    *reinterpret_cast<uint4*>(obase + r * o_ss + 8 * u) = v;
+  }
+}
+
 // Per-workgroup constants of the key loop.
 template <typename T>
 struct LoopCtx {
@@ -541,23 +572,16 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
     }
   }
 
-  // ---- epilogue: O = O / l, statistics at the true max
+  // ---- epilogue: O = O / l (through LDS, free since the loop's last
+  // barrier), statistics at the true max
   const float lref = xhalf_sum(lsum);
-  if (!row_ok) return;
   const float inv = lref > 0.f ? 1.f / lref : 0.f;
-  const int64_t orow = tl.q_row0 + row;
-  T* op = static_cast<T*>(p.o) + tl.b * p.o_sb + tl.h * p.o_sh + orow * p.o_ss;
-#pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt) {
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = 32 * dt + 8 * g4 + 4 * hh;
-      T v4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v4[e] = from_f32<T>(oacc[dt][4 * g4 + e] * inv);
-      *reinterpret_cast<uint2*>(op + d) = *reinterpret_cast<const uint2*>(v4);
-    }
+  {
+    T* obase = static_cast<T*>(p.o) + tl.b * p.o_sb + tl.h * p.o_sh + (tl.q_row0 + i0) * p.o_ss;
+    o_tile_store<T, D, kMfmaThreads>(smem, oacc, inv, wave * 32 + l32, hh, obase, p.o_ss, max(min(BM, tl.sq - i0), 0));
   }
+  if (!row_ok) return;
+  const int64_t orow = tl.q_row0 + row;
   if (p.smax || p.ssum) {
     const int64_t so = tl.b * p.st_sb + tl.h * p.st_sh + orow * p.st_ss + 4 * hh;
     const float mnat = m_max == kNegInf ? kNegInf : m_max * kLn2;

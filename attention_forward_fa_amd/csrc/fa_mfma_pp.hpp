@@ -476,23 +476,18 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
   float& m_max = st.m_max;
   float& lsum = st.lsum;
   f32x16 (&oacc)[C::NDT] = st.oacc;
-  // ---- epilogue: O = O / l, statistics at the true max
+  // ---- epilogue: O = O / l (through LDS once the loads past the last block
+  // have landed), statistics at the true max
   const float lref = xhalf_sum(lsum);
-  if (!row_ok) return;
   const float inv = lref > 0.f ? 1.f / lref : 0.f;
-  const int64_t orow = tl.q_row0 + row;
-  T* op = static_cast<T*>(p.o) + tl.b * p.o_sb + tl.h * p.o_sh + orow * p.o_ss;
-#pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt) {
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = 32 * dt + 8 * g4 + 4 * hh;
-      T v4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v4[e] = from_f32<T>(oacc[dt][4 * g4 + e] * inv);
-      *reinterpret_cast<uint2*>(op + d) = *reinterpret_cast<const uint2*>(v4);
-    }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  __syncthreads();
+  {
+    T* obase = static_cast<T*>(p.o) + tl.b * p.o_sb + tl.h * p.o_sh + (tl.q_row0 + i0) * p.o_ss;
+    o_tile_store<T, D, kPpThreads>(smem, oacc, inv, row - i0, hh, obase, p.o_ss, max(min(kPpBM, tl.sq - i0), 0));
   }
+  if (!row_ok) return;
+  const int64_t orow = tl.q_row0 + row;
   if (p.smax || p.ssum) {
     const int64_t so = tl.b * p.st_sb + tl.h * p.st_sh + orow * p.st_ss + 4 * hh;
     const float mnat = m_max == kNegInf ? kNegInf : m_max * kLn2;
