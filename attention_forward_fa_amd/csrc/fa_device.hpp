@@ -69,27 +69,17 @@ __device__ __forceinline__ Tile map_tile(const Params& p, int bid) {
     return t;
   }
   t.h = lin / tph;
-  int r = lin - t.h * tph;
-  const int32_t* pre = p.tile_prefix;
-  const int total = pre[p.nbatch];
-  t.valid = r < total;
-  if (!t.valid) return t;
-  if (p.reverse_tiles) r = total - 1 - r;
-  // largest b with pre[b] <= r (pre is non-decreasing, pre[0] = 0)
-  int lo = 0, hi = p.nbatch - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (pre[mid] <= r) lo = mid; else hi = mid - 1;
-  }
-  t.b = lo;
-  t.qt = r - pre[lo];
-  // clamp so a corrupt cu_seqlens can only shrink the work, never reach outside [0, T)
-  const int q0 = min(max(p.cu_q[lo], 0), p.tq), q1 = min(max(p.cu_q[lo + 1], q0), p.tq);
-  const int k0 = min(max(p.cu_kv[lo], 0), p.tkv), k1 = min(max(p.cu_kv[lo + 1], k0), p.tkv);
-  t.q_row0 = q0;
-  t.kv_row0 = k0;
-  t.sq = q1 - q0;
-  t.skv = k1 - k0;
+  const int r = lin - t.h * tph;
+  // one 32-byte entry of the tile map (built on the device before this kernel)
+  const int4* e = reinterpret_cast<const int4*>(p.tile_map) + 2 * r;
+  const int4 e0 = e[0], e1 = e[1];
+  t.valid = e1.z != 0;
+  t.b = e0.x;
+  t.qt = e0.y;
+  t.q_row0 = e0.z;
+  t.kv_row0 = e0.w;
+  t.sq = e1.x;
+  t.skv = e1.y;
   return t;
 }
 

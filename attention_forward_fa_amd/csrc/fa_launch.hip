@@ -7,9 +7,11 @@
 
 namespace fa {
 
-// tile_prefix[b] = sum over sequences before b of ceil(rows / bm); one workgroup.
-__global__ void __launch_bounds__(256) varlen_tile_prefix(const int32_t* __restrict__ cu, int total, int nbatch, int bm,
-                                                         int32_t* __restrict__ prefix) {
+// tile_prefix[b] = sum over sequences before b of ceil(rows / bm), then the
+// tile map built from it; one workgroup.
+__global__ void __launch_bounds__(256) varlen_tile_prefix(const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_kv,
+                                                         int total, int tkv, int nbatch, int bm, int tph, int reverse,
+                                                         int32_t* __restrict__ prefix, int32_t* __restrict__ map) {
   __shared__ int part[256];
   const int tid = threadIdx.x;
   const int per = (nbatch + 255) / 256;
@@ -34,6 +36,34 @@ __global__ void __launch_bounds__(256) varlen_tile_prefix(const int32_t* __restr
   }
   if (b1 == nbatch && b0 < b1) prefix[nbatch] = acc;
   if (nbatch == 0 && tid == 0) prefix[0] = 0;
+  __syncthreads();  // the prefix is visible to the whole workgroup
+
+  // The tile map: entry r of the grid's per-head tile index (r < tph) holds
+  // the sequence b, its query tile qt and the clamped row / key ranges of the
+  // tile it runs; heavier (later) tiles first when `reverse`.  Entries past
+  // the total are marked invalid.
+  const int ntiles = prefix[nbatch];
+  const int tq = total;
+  const int32_t* cu_q = cu;
+  for (int r = threadIdx.x; r < tph; r += 256) {
+    int4 e0 = make_int4(0, 0, 0, 0), e1 = make_int4(0, 0, 0, 0);
+    if (r < ntiles) {
+      const int rr = reverse ? ntiles - 1 - r : r;
+      // largest b with prefix[b] <= rr (prefix is non-decreasing, prefix[0] = 0)
+      int lo = 0, hi = nbatch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (prefix[mid] <= rr) lo = mid; else hi = mid - 1;
+      }
+      // clamped so a corrupt cu_seqlens can only shrink the work, never reach outside [0, T)
+      const int q0 = min(max(cu_q[lo], 0), tq), q1 = min(max(cu_q[lo + 1], q0), tq);
+      const int k0 = min(max(cu_kv[lo], 0), tkv), k1 = min(max(cu_kv[lo + 1], k0), tkv);
+      e0 = make_int4(lo, rr - prefix[lo], q0, k0);
+      e1 = make_int4(q1 - q0, k1 - k0, 1, 0);
+    }
+    reinterpret_cast<int4*>(map)[2 * r] = e0;
+    reinterpret_cast<int4*>(map)[2 * r + 1] = e1;
+  }
 }
 
 // pse_off[b] = sum over sequences before b of N * rows_q * rows_kv: where
@@ -169,9 +199,12 @@ extern "C" fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_p
   }
   if (p.varlen) {
     p.tile_prefix = static_cast<int32_t*>(workspace);
-    void* args[] = {(void*)&p.cu_q, (void*)&p.tq, (void*)&p.nbatch, (void*)&plan->bm, (void*)&p.tile_prefix};
+    p.tile_map = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan->ws_map_off);
+    void* args[] = {(void*)&p.cu_q,           (void*)&p.cu_kv,          (void*)&p.tq,      (void*)&p.tkv,
+                    (void*)&p.nbatch,         (void*)&plan->bm,         (void*)&p.tiles_per_head,
+                    (void*)&p.reverse_tiles,  (void*)&p.tile_prefix,    (void*)&p.tile_map};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::varlen_tile_prefix), dim3(1), dim3(256), args, 0, s);
-    if (e != hipSuccess) return runtime_fail("tile prefix launch", e);
+    if (e != hipSuccess) return runtime_fail("tile map launch", e);
     if (p.has_pse) {
       p.pse_off = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + plan->ws_pse_off);
       void* pargs[] = {(void*)&p.cu_q, (void*)&p.cu_kv, (void*)&p.tq, (void*)&p.tkv, (void*)&p.nbatch, (void*)&p.nq,

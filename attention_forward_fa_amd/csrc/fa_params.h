@@ -48,6 +48,7 @@ struct Params {
   const int32_t* cu_q;   // TND only
   const int32_t* cu_kv;  // TND only
   int32_t* tile_prefix;  // TND only: workspace, [nbatch + 1]
+  int32_t* tile_map;     // TND only: workspace, [tiles_per_head][8] = {b, qt, q0, k0, sq, skv, valid, 0}
   const void* pse;       // may be null: additive position bias, q's element type
   int64_t* pse_off;      // TND with pse: workspace, [nbatch + 1] element offset of each sequence's block
   uint8_t* mask_cls;     // with a mask: workspace, class of every (mask slice, 128-row tile, 64-key block)

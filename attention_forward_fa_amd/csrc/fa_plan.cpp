@@ -390,6 +390,7 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   p.cu_q = L == L_TND ? static_cast<const int32_t*>(cu_seqlens_q->data) : nullptr;
   p.cu_kv = L == L_TND ? static_cast<const int32_t*>(cu_seqlens_kv->data) : nullptr;
   p.tile_prefix = nullptr;  // set from the workspace in phase 2
+  p.tile_map = nullptr;
   p.q_sb = q.sb; p.q_ss = q.ss; p.q_sh = q.sh;
   p.k_sb = k.sb; p.k_ss = k.ss; p.k_sh = k.sh;
   p.v_sb = v.sb; p.v_ss = v.ss; p.v_sh = v.sh;
@@ -467,14 +468,17 @@ extern "C" fa_status fa_fwd_get_workspace_size(
 
   const int64_t bm = pl->bm;
   int64_t tiles, wg;
-  // Workspace: [tile prefix, int32, TND] [pse block offsets, int64, TND with
-  // pse] [mask block classes, u8, with a mask], each part 16-byte aligned.
+  // Workspace: [tile prefix, int32, TND] [tile map, 8 x int32 per tile, TND]
+  // [pse block offsets, int64, TND with pse] [mask block classes, u8, with a
+  // mask], each part 16-byte aligned.
   uint64_t ws = 0;
-  pl->ws_pse_off = pl->ws_cls_off = 0;
+  pl->ws_map_off = pl->ws_pse_off = pl->ws_cls_off = 0;
   if (p.varlen) {
     tiles = cdiv(q.s, bm) + nbatch;
     wg = q.s > 0 ? tiles * q.n : 0;
     ws = (uint64_t)(nbatch + 1) * sizeof(int32_t);
+    pl->ws_map_off = (ws + 15) / 16 * 16;
+    ws = pl->ws_map_off + (uint64_t)tiles * 8 * sizeof(int32_t);
     if (p.has_pse) {
       pl->ws_pse_off = (ws + 15) / 16 * 16;
       ws = pl->ws_pse_off + (uint64_t)(nbatch + 1) * sizeof(int64_t);

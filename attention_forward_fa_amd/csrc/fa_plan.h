@@ -12,6 +12,7 @@ struct fa_plan {
   int32_t bm, bn;      // query rows and keys per tile step
   int32_t block;       // threads per workgroup
   uint64_t ws_bytes;   // device workspace phase 2 needs
+  uint64_t ws_map_off; // byte offset of the TND tile map in the workspace
   uint64_t ws_pse_off; // byte offset of the TND pse block offsets in the workspace
   uint64_t ws_cls_off; // byte offset of the mask block classes in the workspace
 };

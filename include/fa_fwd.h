@@ -149,10 +149,14 @@ typedef int32_t fa_status;
  *                       m = sink, l = 1 with a finite sink).
  *   attention_out       output, q's dtype, q's layout with last dim Dv.  Rows
  *                       with no kept key are 0.  Rounded to nearest even.
- *   workspace_size      host out: bytes of device workspace phase 2 needs
- *                       (0 for dense layouts; for TND 4 (B+1) bytes, rounded
- *                       up to 8 and followed by 8 (B+1) more with real_shift,
- *                       in which case the workspace must be 8-byte aligned).
+ *   workspace_size      host out: bytes of device workspace phase 2 needs,
+ *                       16-byte aligned parts: for TND the tile prefix
+ *                       (4 (B+1) bytes) and a 32-byte tile-map entry per
+ *                       tile of the grid, then 8 (B+1) bytes of pse block
+ *                       offsets with a TND real_shift; with atten_mask one
+ *                       class byte per (mask slice, 128-row tile, 64-key
+ *                       block), padded to 16.  0 for a dense call without a
+ *                       mask.  The workspace must be 16-byte aligned.
  *   plan                host out: a new plan, to be released with
  *                       fa_plan_destroy().  It records the tensors' device
  *                       addresses; it may be executed any number of times.

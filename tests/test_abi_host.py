@@ -103,7 +103,7 @@ def test_varlen_plan_workspace():
     smax = desc([N, T, 8], F32)
     st, ws, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND", causal=1, smax=smax, ssum=smax)
     assert st == 0, _lib.last_error_message()
-    assert ws == 4 * 17
+    assert ws == 80 + 80 * 32  # tile prefix (17 int32 -> 80 bytes) + a 32-byte map entry per tile (64 + 16)
     d = describe(pl)
     assert "varlen=1" in d and "grid=1920" in d and "reverse=1" in d, d  # (64 + 16) 128-row tiles x 24 heads
     _lib.fa_plan_destroy(pl)
@@ -308,13 +308,14 @@ def test_mask_class_table_in_workspace():
     st, ws, pl = plan(qq, qq, qq, qq, mask=desc([4000, 4000], U8))
     assert st == 0 and ws == (32 * 63 + 15) // 16 * 16, ws
     _lib.fa_plan_destroy(pl)
-    # TND: tile prefix (6 int32 -> 32 bytes), then the 2-D mask's table (8 x 11 -> 96)
+    # TND: tile prefix (6 int32 -> 32 bytes), tile map (8 + 5 tiles x 32 bytes), then the
+    # 2-D mask's table (8 x 11 -> 96)
     T, N = 1000, 4
     qt = desc([T, N, 128])
     cu = desc([6], I32)
     st, ws, pl = plan(qt, qt, qt, qt, cuq=cu, cuk=cu, layout=b"TND", mask=desc([1000, 700], U8))
     assert st == 0, _lib.last_error_message()
-    assert ws == 32 + 96, ws
+    assert ws == 32 + 13 * 32 + 96, ws
     _lib.fa_plan_destroy(pl)
     # no mask: no table
     st, ws, pl = plan(q, k, v, o)
@@ -329,9 +330,9 @@ def test_phase2_argument_errors_without_launch():
     q = desc([T, N, 128])
     cu = desc([5], I32)
     st, ws, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND")
-    assert st == 0 and ws == 20
+    assert st == 0 and ws == 32 + (8 + 4) * 32  # tile prefix (5 int32) + map (12 tiles)
     assert L.fa_fwd(None, 0, pl, None) == 561201
-    assert L.fa_fwd(ctypes.c_void_p(ADDR), 19, pl, None) == 561201
+    assert L.fa_fwd(ctypes.c_void_p(ADDR), ws - 1, pl, None) == 561201
     assert "workspace" in _lib.last_error_message()
     _lib.fa_plan_destroy(pl)
 
@@ -465,7 +466,7 @@ def test_pse_tnd_workspace():
     cu = desc([6], I32)
     st, ws, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND", pse=desc([12345]))
     assert st == 0, _lib.last_error_message()
-    assert ws == 32 + 8 * 6  # tile prefix (6 int32, padded to 16 bytes) + 6 int64 offsets
+    assert ws == 32 + 13 * 32 + 8 * 6  # tile prefix (6 int32 -> 32 bytes), map (13 tiles), 6 int64 offsets
     _lib.fa_plan_destroy(pl)
     st, _, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND", pse=desc([10, 10]))
     assert st == 561103 and pl is None
