@@ -100,12 +100,16 @@ __global__ void __launch_bounds__(256) varlen_pse_prefix(const int32_t* __restri
 
 // Mask block classes: one workgroup per (slice, 128-row tile, 64-key block).
 // A position counts when it lies inside [rows, cols); for the 2-D TND mask
-// (outside_excluded) positions beyond it count as excluded, as the kernels
-// read them.  Class: all counted positions kept, all excluded, or mixed.
+// (outside_excluded) positions beyond it count as excluded by the mask, as
+// the kernels read them.  With the window active (band), a position the
+// window excludes is excluded whatever the mask says.  Class: EXCLUDED when
+// no counted position survives both; KEPT when the mask excludes no position
+// the window keeps (the block then needs no mask bytes, only the window
+// tests the kernels do anyway); MIXED otherwise.
 __global__ void __launch_bounds__(256) mask_classify(const uint8_t* __restrict__ mask, int64_t m_sb, int64_t m_sh,
                                                      int64_t m_sq, int64_t m_sk, int nh, int rows, int cols,
-                                                     int tiles, int kblocks, int outside_excluded, int vec,
-                                                     uint8_t* __restrict__ cls) {
+                                                     int tiles, int kblocks, int outside_excluded, int vec, int band,
+                                                     int pre, int next, uint8_t* __restrict__ cls) {
   const int64_t id = blockIdx.x;
   const int kb = (int)(id % kblocks);
   const int t = (int)((id / kblocks) % tiles);
@@ -115,32 +119,38 @@ __global__ void __launch_bounds__(256) mask_classify(const uint8_t* __restrict__
   // thread: row tid / 2 of the tile, keys 32 (tid % 2) .. +31 of the block
   const int r = t * kClsRows + (threadIdx.x >> 1);
   const int c0 = kb * kClsKeys + 32 * (threadIdx.x & 1);
-  bool kept = false, excl = false;
-  if (vec && r < rows && c0 + 32 <= cols) {
+  // the window keeps keys [r - pre, r + next] of row r
+  const bool win_all = !band || (c0 + 31 - r <= next && r - c0 <= pre);
+  const bool win_none = band && (c0 - r > next || r - (c0 + 31) > pre);
+  bool alive = false, relevant = false;  // kept by both; excluded by the mask only
+  if (win_none) {
+    // nothing in this segment survives the window
+  } else if (win_all && vec && r < rows && c0 + 32 <= cols) {
     // 32 contiguous bytes of the row: two 16-byte loads
     const uint4* src = reinterpret_cast<const uint4*>(base + (int64_t)r * m_sq + c0);
     const uint4 a = src[0], b = src[1];
     const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      kept |= ((w[i] - 0x01010101u) & ~w[i] & 0x80808080u) != 0;  // some byte is 0
-      excl |= w[i] != 0;
+      alive |= ((w[i] - 0x01010101u) & ~w[i] & 0x80808080u) != 0;  // some byte is 0
+      relevant |= w[i] != 0;
     }
   } else {
     for (int c = c0; c < c0 + 32; ++c) {
+      const bool win = !band || (c - r <= next && r - c <= pre);
       const bool inside = r < rows && c < cols;
       if (inside) {
         const bool e = base[(int64_t)r * m_sq + (int64_t)c * m_sk] != 0;
-        kept |= !e;
-        excl |= e;
+        alive |= !e && win;
+        relevant |= e && win;
       } else if (outside_excluded) {
-        excl = true;
+        relevant |= win;
       }
     }
   }
-  const int any_kept = __syncthreads_or(kept);
-  const int any_excl = __syncthreads_or(excl);
-  if (threadIdx.x == 0) cls[id] = any_kept ? (any_excl ? CLS_MIXED : CLS_KEPT) : CLS_EXCLUDED;
+  const int any_alive = __syncthreads_or(alive);
+  const int any_relevant = __syncthreads_or(relevant);
+  if (threadIdx.x == 0) cls[id] = any_alive ? (any_relevant ? CLS_MIXED : CLS_KEPT) : CLS_EXCLUDED;
 }
 
 }  // namespace fa
@@ -191,7 +201,7 @@ extern "C" fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_p
     if (blocks > 0) {
       void* cargs[] = {(void*)&p.mask, (void*)&p.m_sb, (void*)&p.m_sh, (void*)&p.m_sq, (void*)&p.m_sk, (void*)&p.cls_nh,
                        (void*)&rows, (void*)&cols, (void*)&p.cls_tiles, (void*)&p.cls_kblocks, (void*)&outside,
-                       (void*)&vec, (void*)&p.mask_cls};
+                       (void*)&vec, (void*)&p.band, (void*)&p.pre, (void*)&p.next, (void*)&p.mask_cls};
       hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::mask_classify), dim3((unsigned)blocks),
                                      dim3(256), cargs, 0, s);
       if (e != hipSuccess) return runtime_fail("mask classification launch", e);
