@@ -19,10 +19,9 @@
 // operand reads are issued four MFMAs ahead of their use.
 //
 // K and V: NSLOT slots, block b in slot b % NSLOT.  In step b each group
-// loads its share of block b + NSLOT - 1 right after the last matrix
-// instruction of its M phase (the loads go out while those drain, and no
-// softmax phase carries them); block b - 1, whose slot they fill, was read
-// for the last time in step b - 1.  Every step issues the same loads (past
+// loads its share of block b + NSLOT - 1 during its M phase, the loads spread
+// evenly between the matrix instructions (no softmax phase carries them);
+// block b - 1, whose slot they fill, was read for the last time in step b - 1.  Every step issues the same loads (past
 // the last block they read zeros into a free slot), and the end of each odd
 // phase waits for all but the newest NSLOT - 3 blocks, so block b + 2 is in
 // LDS before phase 2b + 2.
@@ -85,40 +84,43 @@ struct PpState {
   float m_ref, m_max, lsum;
 };
 
-// All 512 threads: K (+ Krope) and V of the block at jb into `slot`.  Load n
-// of wave w fills LDS units [64 (8n + w), +64) of each part; rows past the
-// sequence end (or a block past the last) read as zeros.
+// All 512 threads, load `idx` of the LPB that stage the K (+ Krope) and V of
+// the block at jb into `slot`: load n of a part, from wave w, fills LDS units
+// [64 (8n + w), +64) of that part; rows past the sequence end (or a block past
+// the last) read as zeros.
 template <typename T, int D, int DR>
-__device__ __forceinline__ void pp_stage(char* __restrict__ slot, int jb, const PpCtx<T>& x) {
+__device__ __forceinline__ void pp_stage_one(char* __restrict__ slot, int jb, const PpCtx<T>& x, int idx) {
   using C = PpCfg<T, D, DR>;
   jb = __builtin_amdgcn_readfirstlane(jb);  // uniform: the descriptors stay scalar
   const int64_t rows = max(min(x.skv - jb, C::BN), 0);
   const int64_t jbc = min(jb, x.skv);  // keeps the base inside the tensor
-  const T* kb = x.kbase + jbc * (x.krow_b / (int64_t)sizeof(T));
-#pragma unroll
-  for (int n = 0; n < C::K_LOADS; ++n) {
-    const int unit = 64 * (8 * n + x.wave) + x.lane;
+  if (idx < C::K_LOADS) {
+    const T* kb = x.kbase + jbc * (x.krow_b / (int64_t)sizeof(T));
+    const int unit = 64 * (8 * idx + x.wave) + x.lane;
     const int r = unit / C::KU, u = k_swz(r, unit % C::KU);
-    dma16(kb, rows * x.krow_b, (lds_void*)(slot + 1024 * (8 * n + x.wave)), (uint32_t)(r * x.krow_b + u * 16));
-  }
-  if constexpr (DR > 0) {
+    dma16(kb, rows * x.krow_b, (lds_void*)(slot + 1024 * (8 * idx + x.wave)), (uint32_t)(r * x.krow_b + u * 16));
+  } else if (DR > 0 && idx < C::K_LOADS + C::KR_LOADS) {
+    const int n = idx - C::K_LOADS;
     const T* krb = x.krbase + jbc * (x.krrow_b / (int64_t)sizeof(T));
-#pragma unroll
-    for (int n = 0; n < C::KR_LOADS; ++n) {
-      const int unit = 64 * (8 * n + x.wave) + x.lane;
-      const int r = unit / C::KRU, u = k_swz(r, unit % C::KRU);
-      dma16(krb, rows * x.krrow_b, (lds_void*)(slot + C::KR_OFF + 1024 * (8 * n + x.wave)),
-            (uint32_t)(r * x.krrow_b + u * 16));
-    }
-  }
-  const T* vb = x.vbase + jbc * (x.vrow_b / (int64_t)sizeof(T));
-#pragma unroll
-  for (int n = 0; n < C::V_LOADS; ++n) {
+    const int unit = 64 * (8 * n + x.wave) + x.lane;
+    const int r = unit / C::KRU, u = k_swz(r, unit % C::KRU);
+    dma16(krb, rows * x.krrow_b, (lds_void*)(slot + C::KR_OFF + 1024 * (8 * n + x.wave)),
+          (uint32_t)(r * x.krrow_b + u * 16));
+  } else {
+    const int n = idx - C::K_LOADS - C::KR_LOADS;
+    const T* vb = x.vbase + jbc * (x.vrow_b / (int64_t)sizeof(T));
     const int unit = 64 * (8 * n + x.wave) + x.lane;
     const int r = unit / C::VU, u = v_swz<C::VU>(r, unit % C::VU);
     dma16(vb, rows * x.vrow_b, (lds_void*)(slot + C::V_OFF + 1024 * (8 * n + x.wave)),
           (uint32_t)(r * x.vrow_b + u * 16));
   }
+}
+
+// All LPB loads of the block at jb into `slot`.
+template <typename T, int D, int DR>
+__device__ __forceinline__ void pp_stage(char* __restrict__ slot, int jb, const PpCtx<T>& x) {
+#pragma unroll
+  for (int n = 0; n < PpCfg<T, D, DR>::LPB; ++n) pp_stage_one<T, D, DR>(slot, jb, x, n);
 }
 
 // S^T = K Q^T for the block in `slot` (64 keys x this wave's 32 rows).
@@ -198,8 +200,11 @@ __device__ __forceinline__ void pp_mphase(const char* __restrict__ kslot, const 
         const int q = j - NS, ts = q / C::NDT;
         oacc[q % C::NDT] = mfma32<T>(a[j], pk[ts >> 1][ts & 1], oacc[q % C::NDT]);
       }
+      // the next block's loads, spread evenly between the MFMAs
+#pragma unroll
+      for (int n = 0; n < C::LPB; ++n)
+        if (j == (n + 1) * (NS + NP) / (C::LPB + 1)) pp_stage_one<T, D, DR>(fill, jfill, x, n);
     }
-    pp_stage<T, D, DR>(fill, jfill, x);
     // keep the reads kPpAhead MFMAs ahead (the scheduler would pull them back)
     __builtin_amdgcn_sched_group_barrier(0x100, kPpAhead, 0);
 #pragma unroll
@@ -210,9 +215,10 @@ __device__ __forceinline__ void pp_mphase(const char* __restrict__ kslot, const 
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       else if (n < NS + NP)
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int m = 0; m < C::LPB; ++m)
+        if (j == (m + 1) * (NS + NP) / (C::LPB + 1)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     }
-    // the loads go out after the last MFMA
-    __builtin_amdgcn_sched_group_barrier(0x010, C::LPB, 0);
     return;
   }
   pp_stage<T, D, DR>(fill, jfill, x);
