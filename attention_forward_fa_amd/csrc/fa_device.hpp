@@ -38,6 +38,7 @@ struct Tile {
   int64_t q_row0;     // first global row of this sequence in q / o (TND), else 0
   int64_t kv_row0;    // first global row of this sequence in k / v (TND), else 0
   int sq, skv;        // rows of this sequence
+  int split;          // key range of a split grid (0 otherwise)
   bool valid;
 };
 
@@ -56,8 +57,13 @@ __device__ __forceinline__ Tile map_tile(const Params& p, int bid) {
   const int lin = xcd_linear_id(bid, p.num_wg);
   const int tph = p.tiles_per_head;
   if (!p.varlen) {
-    const int bh = lin / tph;
-    const int r = lin - bh * tph;
+    // (sequence, head), then key range, then query tile: the tiles that
+    // share one key range of one head are adjacent
+    const int per_bh = tph * p.kv_splits;
+    const int bh = lin / per_bh;
+    int r = lin - bh * per_bh;
+    t.split = r / tph;
+    r -= t.split * tph;
     t.b = bh / p.nq;
     t.h = bh - t.b * p.nq;
     t.qt = p.reverse_tiles ? tph - 1 - r : r;
@@ -69,6 +75,7 @@ __device__ __forceinline__ Tile map_tile(const Params& p, int bid) {
     return t;
   }
   t.h = lin / tph;
+  t.split = 0;
   const int r = lin - t.h * tph;
   // one 32-byte entry of the tile map (built on the device before this kernel)
   const int4* e = reinterpret_cast<const int4*>(p.tile_map) + 2 * r;

@@ -223,6 +223,10 @@ extern "C" fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_p
       if (e != hipSuccess) return runtime_fail("pse prefix launch", e);
     }
   }
+  if (p.kv_splits > 1) {
+    p.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->ws_part_off);
+    p.part_ml = p.part_o + (int64_t)p.kv_splits * p.nbatch * p.nq * p.sq * p.dv;
+  }
   hipError_t e;
   if (plan->kind == fa::KERNEL_MFMA_PP)
     e = plan->dtype == FA_DTYPE_BF16 ? fa::launch_mfma_pp_bf16(p, s) : fa::launch_mfma_pp_f16(p, s);
@@ -231,5 +235,9 @@ extern "C" fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_p
   else
     e = fa::launch_generic(p, plan->dtype, s);
   if (e != hipSuccess) return runtime_fail("forward kernel launch", e);
+  if (p.kv_splits > 1) {
+    e = fa::launch_split_merge(p, plan->dtype, s);
+    if (e != hipSuccess) return runtime_fail("key split merge launch", e);
+  }
   return FA_OK;
 }

@@ -16,6 +16,7 @@
 
 #include "fa_device.hpp"
 #include "fa_fwd.h"
+#include "fa_launch.h"
 #include "fa_merge.h"
 
 namespace fa {
@@ -153,6 +154,84 @@ int merge_launch(const MergeParams& mp, int32_t dtype, void* stream) {
   }
   return (int)hipLaunchKernel(fn, dim3((unsigned)((rows + 3) / 4)), dim3(256), args, 0,
                               static_cast<hipStream_t>(stream));
+}
+
+// Key-split merge of the 4-wave kernel: the same combination over the
+// kv_splits fp32 partial results of each query row (workspace, rows in
+// (sequence, head, row) order), written to the output in its layout and dtype
+// with the statistics.  Thread = (row, 8-element chunk).
+template <typename T>
+__global__ void __launch_bounds__(256) fa_split_merge_kernel(const Params p) {
+  const int cpr = p.dv / 8;
+  const int64_t rows = (int64_t)p.nbatch * p.nq * p.sq;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = t / cpr;
+  const int chunk = (int)(t - r * cpr);
+  if (r >= rows) return;
+  const int64_t bh = r / p.sq;
+  const int s = (int)(r - bh * p.sq);
+  const int b = (int)(bh / p.nq), h = (int)(bh - (int64_t)b * p.nq);
+  float w[kMaxKvSplits], mc[kMaxKvSplits];
+  float m = kNegInf;
+#pragma unroll
+  for (int c = 0; c < kMaxKvSplits; ++c) {
+    if (c < p.kv_splits) {
+      const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + 2 * (c * rows + r));
+      mc[c] = ml.x;
+      w[c] = ml.y;
+      m = fmaxf(m, ml.x);
+    }
+  }
+  float l = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMaxKvSplits; ++c) {
+    if (c < p.kv_splits) {
+      w[c] = mc[c] == kNegInf ? 0.f : expf(mc[c] - m) * w[c];
+      l += w[c];
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kMaxKvSplits; ++c) {
+    if (c < p.kv_splits) {
+      const float4* pc = reinterpret_cast<const float4*>(p.part_o + (c * rows + r) * p.dv + 8 * chunk);
+      const float4 a = pc[0], e = pc[1];
+      acc[0] = fmaf(w[c], a.x, acc[0]);
+      acc[1] = fmaf(w[c], a.y, acc[1]);
+      acc[2] = fmaf(w[c], a.z, acc[2]);
+      acc[3] = fmaf(w[c], a.w, acc[3]);
+      acc[4] = fmaf(w[c], e.x, acc[4]);
+      acc[5] = fmaf(w[c], e.y, acc[5]);
+      acc[6] = fmaf(w[c], e.z, acc[6]);
+      acc[7] = fmaf(w[c], e.w, acc[7]);
+    }
+  }
+  T res[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) res[i] = from_f32<T>(acc[i] * inv);
+  T* o = static_cast<T*>(p.o) + b * p.o_sb + h * p.o_sh + s * p.o_ss + 8 * chunk;
+  *reinterpret_cast<uint4*>(o) = *reinterpret_cast<const uint4*>(res);
+  if (chunk == 0) {
+    const int64_t so = b * p.st_sb + h * p.st_sh + s * p.st_ss;
+    if (p.smax) {
+      reinterpret_cast<float4*>(p.smax + so)[0] = make_float4(m, m, m, m);
+      reinterpret_cast<float4*>(p.smax + so)[1] = make_float4(m, m, m, m);
+    }
+    if (p.ssum) {
+      reinterpret_cast<float4*>(p.ssum + so)[0] = make_float4(l, l, l, l);
+      reinterpret_cast<float4*>(p.ssum + so)[1] = make_float4(l, l, l, l);
+    }
+  }
+}
+
+hipError_t launch_split_merge(const Params& p, int dtype, hipStream_t s) {
+  const int64_t threads = (int64_t)p.nbatch * p.nq * p.sq * (p.dv / 8);
+  if (threads == 0) return hipSuccess;
+  void* args[] = {const_cast<Params*>(&p)};
+  const void* fn = dtype == FA_DTYPE_BF16 ? reinterpret_cast<const void*>(&fa_split_merge_kernel<__bf16>)
+                                          : reinterpret_cast<const void*>(&fa_split_merge_kernel<_Float16>);
+  return hipLaunchKernel(fn, dim3((unsigned)((threads + 255) / 256)), dim3(256), args, 0, s);
 }
 
 }  // namespace fa

@@ -493,6 +493,10 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   const int last_row = min(i0 + BM, tl.sq) - 1;
   int kv_lo, kv_hi;
   key_range(p, i0, last_row, tl.skv, &kv_lo, &kv_hi);
+  if (p.kv_splits > 1) {  // this workgroup's key range (whole key blocks)
+    kv_lo = max(kv_lo, tl.split * p.split_keys);
+    kv_hi = min(kv_hi, (tl.split + 1) * p.split_keys - 1);
+  }
   const int jb0 = (kv_lo / BN) * BN;
   const int nblocks = (kv_hi >= kv_lo && last_row >= i0) ? (kv_hi - jb0) / BN + 1 : 0;
 
@@ -500,7 +504,7 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   float m_ref = kNegInf;  // reference max of the exponentials
   float m_max = kNegInf;  // true running max (for softmaxMax)
   float lsum = 0.f;       // this half-wave's part of sum_j 2^(t_j - m_ref)
-  if (p.has_sink) {
+  if (p.has_sink && tl.split == 0) {  // the sink term belongs to one key range
     const float sk = p.sink[tl.h];
     if (sk > kNegInf) {
       m_ref = m_max = sk * kLog2e;
@@ -576,6 +580,26 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   // barrier), statistics at the true max
   const float lref = xhalf_sum(lsum);
   const float inv = lref > 0.f ? 1.f / lref : 0.f;
+  if (p.kv_splits > 1) {
+    // partial result over this key range, in fp32: O_c = O / l_c and the
+    // range's statistics (max, sum at that max), merged by a later pass
+    if (!row_ok) return;
+    const int64_t prow = ((int64_t)(tl.split * p.nbatch + tl.b) * p.nq + tl.h) * p.sq + row;
+    float* po = p.part_o + prow * D;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(po + 32 * dt + 8 * g4 + 4 * hh) =
+            make_float4(oacc[dt][4 * g4] * inv, oacc[dt][4 * g4 + 1] * inv, oacc[dt][4 * g4 + 2] * inv,
+                        oacc[dt][4 * g4 + 3] * inv);
+    if (hh == 0) {
+      const float mnat = m_max == kNegInf ? kNegInf : m_max * kLn2;
+      const float ltrue = lref > 0.f ? lref * fast_exp2(m_ref - m_max) : 0.f;
+      *reinterpret_cast<float2*>(p.part_ml + 2 * prow) = make_float2(mnat, ltrue);
+    }
+    return;
+  }
   {
     T* obase = static_cast<T*>(p.o) + tl.b * p.o_sb + tl.h * p.o_sh + (tl.q_row0 + i0) * p.o_ss;
     o_tile_store<T, D, kMfmaThreads>(smem, oacc, inv, wave * 32 + l32, hh, obase, p.o_ss, max(min(BM, tl.sq - i0), 0));

@@ -25,6 +25,14 @@ enum MaskClass : uint8_t { CLS_KEPT = 0, CLS_EXCLUDED = 1, CLS_MIXED = 2 };
 constexpr int kMfmaBM = 128;
 constexpr int kMfmaBN = 64;
 constexpr int kMfmaThreads = 256;
+// Key split of the 4-wave kernel: a grid with fewer workgroups than the
+// chip holds at once (2 per compute unit, 256 units) gives each query tile up
+// to kMaxKvSplits workgroups over disjoint key ranges of at least
+// kMinSplitBlocks key blocks, then merges their partial results.
+constexpr int kNumCUs = 256;
+constexpr int kMaxKvSplits = 4;
+constexpr int kWgSlots = 2 * kNumCUs;
+constexpr int kMinSplitBlocks = 8;
 // Tile of the two-group matrix-core kernel: 8 wavefronts, 256 query rows.
 constexpr int kMfmaPpBM = 256;
 constexpr int kMfmaPpThreads = 512;
@@ -52,6 +60,8 @@ struct Params {
   const void* pse;       // may be null: additive position bias, q's element type
   int64_t* pse_off;      // TND with pse: workspace, [nbatch + 1] element offset of each sequence's block
   uint8_t* mask_cls;     // with a mask: workspace, class of every (mask slice, 128-row tile, 64-key block)
+  float* part_o;         // key split: workspace, [kv_splits][nbatch * nq * sq][dv] normalised partial outputs
+  float* part_ml;        // key split: workspace, [kv_splits][nbatch * nq * sq][2] = {max, sum}, natural-log units
 
   // element strides: batch, row (sequence position / token), head
   int64_t q_sb, q_ss, q_sh;
@@ -88,6 +98,8 @@ struct Params {
   int32_t tiles_per_head;   // dense: ceil(sq / BM); TND: ceil(tq / BM) + nbatch (upper bound)
   int32_t num_wg;           // grid size
   int32_t reverse_tiles;    // schedule later (heavier) query tiles first
+  int32_t kv_splits;        // dense, 4-wave kernel: workgroups per query tile, each over one key range (1 = off)
+  int32_t split_keys;       // keys per range (a multiple of the key block); range c = [c * split_keys, +split_keys)
 };
 
 }  // namespace fa

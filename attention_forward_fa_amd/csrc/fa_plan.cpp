@@ -135,12 +135,12 @@ extern "C" int32_t fa_plan_describe(const fa_plan* plan, char* buf, size_t len) 
   const int n = snprintf(buf, len,
                          "kernel=%s dtype=%s d=%d dr=%d dv=%d bm=%d bn=%d grid=%d block=%d ws=%llu "
                          "varlen=%d band=%d pre=%d next=%d mask=%d sink=%d "
-                         "nq=%d nkv=%d tiles_per_head=%d reverse=%d pse=%d pse_lds=%d",
+                         "nq=%d nkv=%d tiles_per_head=%d reverse=%d pse=%d pse_lds=%d kv_splits=%d",
                          plan->kind == fa::KERNEL_MFMA_PP ? "mfma_pp" : (plan->kind == fa::KERNEL_MFMA ? "mfma" : "generic"),
                          dtype_name(plan->dtype), p.d, p.dr,
                          p.dv, plan->bm, plan->bn, p.num_wg, plan->block, (unsigned long long)plan->ws_bytes,
                          p.varlen, p.band, p.pre, p.next, p.has_mask, p.has_sink, p.nq, p.nkv,
-                         p.tiles_per_head, p.reverse_tiles, p.has_pse, p.pse_lds);
+                         p.tiles_per_head, p.reverse_tiles, p.has_pse, p.pse_lds, p.kv_splits);
   return n;
 }
 
@@ -346,14 +346,17 @@ extern "C" fa_status fa_fwd_get_workspace_size(
                        (!query_rope || (vec_ok(query_rope->data, qr) && vec_ok(key_rope->data, kr))) && stats_vec;
   // Family: the two-group (ping-pong) matrix-core kernel for long dense
   // sequences at D = 128 without rope whose window cuts at most the causal
-  // side (it measures faster there: one K / V stream serves 256 query rows);
-  // the four-wave matrix-core kernel wherever else it applies (short or
-  // varlen sequences, rope, sliding windows, D = 64); the generic kernel for
-  // everything else.  FA_FWD_KERNEL=mfma|pp|generic forces a family (tests and
+  // side, with at least one workgroup per compute unit (it measures faster
+  // there: one K / V stream serves 256 query rows); the four-wave
+  // matrix-core kernel wherever else it applies (short or varlen sequences,
+  // rope, sliding windows, D = 64, grids too small for the two-group kernel,
+  // which it may split along the keys); the generic kernel for everything
+  // else.  FA_FWD_KERNEL=mfma|pp|generic forces a family (tests and
   // benchmarks); forcing a matrix-core family on a shape it does not cover is
   // an error.
   const bool pp_pref = q.d == 128 && dr == 0 && L != L_TND && q.s >= 1024 && k.s >= 1024 &&
-                       (!band || pre >= k.s - 1) && !real_shift;
+                       (!band || pre >= k.s - 1) && !real_shift &&
+                       q.b * q.n * cdiv(q.s, fa::kMfmaPpBM) >= fa::kNumCUs;
   int kind = mfma_ok ? (pp_pref ? fa::KERNEL_MFMA_PP : fa::KERNEL_MFMA) : fa::KERNEL_GENERIC;
   if (const char* force = getenv("FA_FWD_KERNEL")) {
     if (!strcmp(force, "generic")) {
@@ -487,6 +490,38 @@ extern "C" fa_status fa_fwd_get_workspace_size(
     tiles = cdiv(q.s, bm);
     wg = tiles * q.b * q.n;
   }
+  // Key split (dense, 4-wave kernel): a grid that leaves workgroup slots of
+  // the chip empty gets up to kMaxKvSplits workgroups per query tile, each
+  // over kv_splits-th of the keys (whole key blocks, at least kMinSplitBlocks
+  // of them), and a merge pass.  FA_FWD_KV_SPLIT=n forces n ranges (1 = off;
+  // tests and benchmarks).
+  p.kv_splits = 1;
+  p.split_keys = 0;
+  p.part_o = p.part_ml = nullptr;
+  pl->ws_part_off = 0;
+  if (kind == fa::KERNEL_MFMA && !p.varlen && wg > 0 && k.s > 0) {
+    int64_t want = fa::kWgSlots / wg;
+    if (want > fa::kMaxKvSplits) want = fa::kMaxKvSplits;
+    const int64_t max_by_len = k.s / ((int64_t)fa::kMinSplitBlocks * pl->bn);
+    if (want > max_by_len) want = max_by_len;
+    if (const char* force = getenv("FA_FWD_KV_SPLIT")) {
+      char* end = nullptr;
+      const long n = strtol(force, &end, 10);
+      if (force[0] != '\0') {
+        if (*end != '\0' || n < 1 || n > fa::kMaxKvSplits) {
+          delete pl;
+          return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KV_SPLIT='%s' not a count in 1..%d", force, fa::kMaxKvSplits);
+        }
+        want = n;
+      }
+    }
+    if (want >= 2) {
+      const int64_t keys = cdiv(cdiv(k.s, want), pl->bn) * pl->bn;
+      p.kv_splits = (int32_t)cdiv(k.s, keys);
+      p.split_keys = (int32_t)keys;
+      wg *= p.kv_splits;
+    }
+  }
   p.mask_cls = nullptr;
   p.cls_nh = p.cls_tiles = p.cls_kblocks = p.cls_slices = 0;
   if (p.has_mask) {
@@ -512,6 +547,12 @@ extern "C" fa_status fa_fwd_get_workspace_size(
     pl->ws_cls_off = (ws + 15) / 16 * 16;
     // padded to 16 bytes: the kernels read the table a dword at a time
     ws = pl->ws_cls_off + ((uint64_t)nslices * p.cls_tiles * p.cls_kblocks + 15) / 16 * 16;
+  }
+  if (p.kv_splits > 1) {
+    // fp32 partial outputs [kv_splits][rows][dv], then {max, sum} [kv_splits][rows][2]
+    const uint64_t rows = (uint64_t)p.kv_splits * q.b * q.n * q.s;
+    pl->ws_part_off = (ws + 15) / 16 * 16;
+    ws = pl->ws_part_off + rows * (uint64_t)(v.d + 2) * sizeof(float);
   }
   pl->ws_bytes = ws;
   if (wg >= ((int64_t)1 << 31)) {

@@ -15,6 +15,7 @@ struct fa_plan {
   uint64_t ws_map_off; // byte offset of the TND tile map in the workspace
   uint64_t ws_pse_off; // byte offset of the TND pse block offsets in the workspace
   uint64_t ws_cls_off; // byte offset of the mask block classes in the workspace
+  uint64_t ws_part_off; // byte offset of the key split's partial outputs (then their statistics)
 };
 
 // Record the message fa_last_error_message() returns on this thread.

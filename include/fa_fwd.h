@@ -155,8 +155,10 @@ typedef int32_t fa_status;
  *                       tile of the grid, then 8 (B+1) bytes of pse block
  *                       offsets with a TND real_shift; with atten_mask one
  *                       class byte per (mask slice, 128-row tile, 64-key
- *                       block), padded to 16.  0 for a dense call without a
- *                       mask.  The workspace must be 16-byte aligned.
+ *                       block), padded to 16; with a key split (below)
+ *                       kv_splits x B x N x Sq x (Dv + 2) fp32 partial
+ *                       results.  0 for a dense call without a mask or key
+ *                       split.  The workspace must be 16-byte aligned.
  *   plan                host out: a new plan, to be released with
  *                       fa_plan_destroy().  It records the tensors' device
  *                       addresses; it may be executed any number of times.
@@ -164,11 +166,17 @@ typedef int32_t fa_status;
  * Kernel choice: a matrix-core kernel when q is F16/BF16, D is 64 or 128,
  * Dr is 0 or 64, Dv == D and every row start is 16-byte aligned (the
  * two-group one for dense Sq, Skv >= 1024 at D = 128 without rope or pse
- * whose window cuts at most the causal side, else the four-wave one);
+ * whose window cuts at most the causal side and whose grid of 256-row tiles
+ * has at least 256 workgroups, else the four-wave one);
  * otherwise the generic one (fp32 dot products on the vector units).  The environment
  * variable FA_FWD_KERNEL = "mfma" | "pp" | "generic", read here, forces a
  * family for testing; forcing one the arguments do not fit returns
- * FA_ERR_UNSUPPORTED.
+ * FA_ERR_UNSUPPORTED.  Key split: a dense four-wave grid of fewer than 512
+ * workgroups (two per compute unit) runs up to 4 workgroups per query tile,
+ * each over a contiguous range of at least 512 keys, and merges their fp32
+ * partial results (the combination fa_fwd_merge states) in a second kernel;
+ * FA_FWD_KV_SPLIT = 1..4 forces the number of ranges (1 = no split), other
+ * values return FA_ERR_UNSUPPORTED.
  *
  * Returns FA_OK, FA_ERR_PARAM_NULLPTR, FA_ERR_PARAM_INVALID or
  * FA_ERR_UNSUPPORTED.  On error *plan is set to NULL.  No device work.

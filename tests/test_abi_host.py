@@ -306,7 +306,9 @@ def test_mask_class_table_in_workspace():
     s = [1, 4000, 2, 128]
     qq = desc(s)
     st, ws, pl = plan(qq, qq, qq, qq, mask=desc([4000, 4000], U8))
-    assert st == 0 and ws == (32 * 63 + 15) // 16 * 16, ws
+    # (64 workgroups: the keys split in 4 ranges, whose fp32 partials follow the table)
+    assert st == 0 and "kv_splits=4" in describe(pl)
+    assert ws == (32 * 63 + 15) // 16 * 16 + 4 * 2 * 4000 * 130 * 4, ws
     _lib.fa_plan_destroy(pl)
     # TND: tile prefix (6 int32 -> 32 bytes), tile map (8 + 5 tiles x 32 bytes), then the
     # 2-D mask's table (8 x 11 -> 96)
@@ -360,7 +362,7 @@ def test_describe_truncates_safely():
     ("d64", "mfma"),
 ])
 def test_family_policy(case, family):
-    S, N = 4096, 4
+    S, N = 4096, 16  # 256 two-group workgroups: one per compute unit
     q = desc([1, N, S, 128 if case != "d64" else 64])
     kw = dict(layout=b"BNSD")
     if case in ("causal", "band"):
@@ -373,6 +375,70 @@ def test_family_policy(case, family):
     d = describe(pl)
     assert f"kernel={family} " in d, d
     _lib.fa_plan_destroy(pl)
+
+
+@pytest.mark.parametrize("pse", [False, True])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_small_dense_grid_splits_keys(pse, causal):
+    # B1 N8 S4096: 128 two-group workgroups would leave half the compute units
+    # idle; 256 four-wave workgroups fill half the slots, so two key ranges
+    B, N, S, D = 1, 8, 4096, 128
+    q = desc([B, N, S, D])
+    kw = dict(layout=b"BNSD", causal=causal, nxt=0 if causal else 2**31 - 1)
+    if pse:
+        kw["pse"] = desc([B, N, S, S])
+    st, ws, pl = plan(q, q, q, q, **kw)
+    assert st == 0, _lib.last_error_message()
+    d = describe(pl)
+    assert "kernel=mfma " in d and "kv_splits=2" in d and "grid=512" in d, d
+    assert ws == 2 * B * N * S * (D + 2) * 4  # fp32 partial outputs and {max, sum}
+    _lib.fa_plan_destroy(pl)
+
+
+@pytest.mark.parametrize("force,skv,splits,grid", [("1", 4096, 1, 256), ("3", 1000, 3, 768), ("4", 4096, 4, 1024),
+                                                   ("2", 100, 2, 512), ("4", 100, 2, 512)])
+def test_forced_key_split(monkeypatch, force, skv, splits, grid):
+    monkeypatch.setenv("FA_FWD_KV_SPLIT", force)
+    B, N, S, D = 1, 8, 4096, 128
+    q, k = desc([B, N, S, D]), desc([B, N, skv, D])
+    st, ws, pl = plan(q, k, k, q, layout=b"BNSD")
+    assert st == 0, _lib.last_error_message()
+    d = describe(pl)
+    assert "kernel=mfma " in d and f"kv_splits={splits} " in d + " " and f"grid={grid} " in d, d
+    assert ws == (splits * B * N * S * (D + 2) * 4 if splits > 1 else 0)
+    _lib.fa_plan_destroy(pl)
+
+
+def test_key_split_limits(monkeypatch):
+    # keys shorter than 8 blocks per range, a full grid, TND and the two-group
+    # kernel never split on their own; bad forced counts are rejected
+    s = [1, 8, 600, 128]
+    st, ws, pl = plan(desc(s), desc(s), desc(s), desc(s), layout=b"BNSD")
+    assert st == 0 and "kv_splits=1" in describe(pl) and ws == 0
+    _lib.fa_plan_destroy(pl)
+    q, k, v, o = c2()
+    monkeypatch.setenv("FA_FWD_KERNEL", "mfma")
+    st, ws, pl = plan(q, k, v, o)
+    assert st == 0 and "kv_splits=1" in describe(pl) and "grid=1536" in describe(pl)
+    _lib.fa_plan_destroy(pl)
+    monkeypatch.setenv("FA_FWD_KERNEL", "pp")
+    monkeypatch.setenv("FA_FWD_KV_SPLIT", "2")
+    st, ws, pl = plan(q, k, v, o)
+    assert st == 0 and "kv_splits=1" in describe(pl) and "kernel=mfma_pp" in describe(pl)
+    _lib.fa_plan_destroy(pl)
+    monkeypatch.delenv("FA_FWD_KERNEL")
+    T = 4096
+    t3 = desc([T, 2, 128])
+    cu = desc([2], I32)
+    st, ws, pl = plan(t3, t3, t3, t3, cuq=cu, cuk=cu, layout=b"TND", causal=1, nxt=0)
+    assert st == 0, _lib.last_error_message()
+    assert "kv_splits=1" in describe(pl)
+    _lib.fa_plan_destroy(pl)
+    for bad in ["0", "5", "two", "-1"]:
+        monkeypatch.setenv("FA_FWD_KV_SPLIT", bad)
+        st, _, pl = plan(desc([1, 8, 4096, 128]), desc([1, 8, 4096, 128]), desc([1, 8, 4096, 128]),
+                         desc([1, 8, 4096, 128]), layout=b"BNSD")
+        assert st == 561103 and pl is None and "FA_FWD_KV_SPLIT" in _lib.last_error_message()
 
 
 def test_small_grid_uses_four_wave_kernel():

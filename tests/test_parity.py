@@ -232,6 +232,80 @@ def test_small_case(name, kernel):
     _report(f"{name}/{kernel}", errs)
 
 
+# ---------------------------------------------------------------------------
+# key split of the four-wave kernel: partial results over key ranges, merged
+# ---------------------------------------------------------------------------
+
+def _split_sink_neg_inf_case(seed):
+    c = synth.dense_case("x", "BSND", 1, 3, 260, 128, "bf16", seed, skv=700, sink=True)
+    c.sink = torch.tensor([float("-inf"), 1.5, -0.5])
+    return c
+
+
+def _split_window_case(seed):
+    """A narrow window: many rows keep no key of some ranges, a few keep none
+    at all (pre + next < 0 is rejected, so the empty rows come from the mask)."""
+    c = synth.dense_case("x", "BNSD", 1, 2, 500, 128, "bf16", seed, skv=600, sink=True)
+    i = torch.arange(500).view(-1, 1)
+    j = torch.arange(600).view(1, -1)
+    m = ((j - i) > 20) | ((i - j) > 90)
+    m[:, :] |= (i >= 480) & (i < 490)  # ten rows with no kept key
+    c.atten_mask = m.to(torch.uint8)
+    c.pre_tokens, c.next_tokens = 90, 20
+    return c
+
+
+SPLIT = {
+    "dense_ragged": lambda: synth.dense_case("x", "BNSD", 2, 3, 201, 128, "bf16", 100, skv=650),
+    "sink_causal_bsnd": lambda: synth.dense_case("x", "BSND", 1, 3, 300, 128, "bf16", 101, sink=True, causal=True),
+    "sink_neg_inf": lambda: _split_sink_neg_inf_case(102),
+    "gqa_fp16_sq_lt_skv": lambda: synth.dense_case("x", "BNSD", 1, 4, 130, 128, "fp16", 103, nkv=2, skv=900),
+    "d64_rope_causal": lambda: synth.dense_case("x", "BSND", 1, 2, 260, 64, "bf16", 104, drope=64, causal=True,
+                                                skv=260),
+    "d128_rope_sink": lambda: synth.dense_case("x", "BNSD", 1, 2, 200, 128, "bf16", 105, drope=64, sink=True,
+                                               skv=520),
+    "pse_lds_causal": lambda: synth.dense_case("x", "BNSD", 1, 2, 300, 128, "bf16", 106, skv=640, pse="full",
+                                               causal=True),
+    "pse_unaligned": lambda: synth.dense_case("x", "BNSD", 1, 2, 140, 128, "bf16", 107, skv=513, pse="bcast"),
+    "block_mask": lambda: _block_mask_case(108, 128, 64, (1, 2)),
+    "window_mask_empty_rows": lambda: _split_window_case(109),
+    "sbh_layout": lambda: _split_sbh_case(110),
+}
+
+
+def _split_sbh_case(seed):
+    base = synth.dense_case("x", "BNSD", 2, 3, 150, 128, "bf16", seed, skv=400, sink=True)
+    return synth.Case(name="sbh", layout="SBH", q=orc.from_bnsd(base.q, "SBH"), k=orc.from_bnsd(base.k, "SBH"),
+                      v=orc.from_bnsd(base.v, "SBH"), scale=base.scale, sink=base.sink)
+
+
+@pytest.mark.parametrize("splits", ["2", "3", "4"])
+@pytest.mark.parametrize("name", sorted(SPLIT))
+def test_key_split(name, splits, monkeypatch):
+    case = SPLIT[name]()
+    print(f"[parity] start split {name} splits={splits} layout={case.layout} q={tuple(case.q.shape)}", flush=True)
+    monkeypatch.setenv("FA_FWD_KV_SPLIT", splits)
+    with pu.forced_kernel("mfma"):
+        errs = pu.compare_case(case, heads=3 if case.layout == "SBH" else None)
+    _report(f"split/{name}/{splits}", errs)
+
+
+def test_key_split_chosen_for_small_grid():
+    """B1 N2: four workgroups, so the plan itself splits the 2100 keys four ways."""
+    case = synth.dense_case("x", "BNSD", 1, 2, 256, 128, "bf16", 111, skv=2100, sink=True)
+    print("[parity] start split auto B1 N2 Sq256 Skv2100", flush=True)
+    g = {k: pu.to_gpu(v, "cuda:0") for k, v in case.tensors().items()}
+    out = torch.empty_like(g["q"])
+    plan = api.ForwardPlan(g["q"], g["k"], g["v"], layout="BNSD", scale=case.scale, head_num=2, sink=g["sink"],
+                           out=out)
+    try:
+        assert "kernel=mfma " in plan.describe() and "kv_splits=4" in plan.describe(), plan.describe()
+    finally:
+        plan.close()
+    errs = pu.compare_case(case)
+    _report("split/auto", errs)
+
+
 @pytest.mark.parametrize("layout", ["BSH", "SBH"])
 def test_hidden_layouts(layout):
     base = synth.dense_case("x", "BNSD", 2, 3, 150, 128, "bf16", 60, causal=True)
