@@ -356,20 +356,29 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
       sacc[0] = mfma32<T>(a0, qf[0], bias[0]);
       sacc[1] = mfma32<T>(a1, qf[0], bias[1]);
     } else if (bk.partial) {
+      // The row keeps keys [lo, hi] (window and sequence end).  Element
+      // e = 32t + 8a + b of this lane is key jb + 4hh + e, so key - lo =
+      // b0 + e, kept iff unsigned(b0 + e) <= span: one add and one compare
+      // per element (an empty range gets a b0 no element can bring back).
+      int lo = 0, hi = x.skv - 1;
+      if (p.band) {
+        lo = max(lo, row - p.pre);
+        hi = min(hi, row + p.next);
+      }
+      const uint32_t span = hi >= lo ? (uint32_t)(hi - lo) : 0u;
+      const uint32_t b0 = hi >= lo ? (uint32_t)(jb + 4 * hh - lo) : 0x80000000u;
       f32x16 bias[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int key = jb + 32 * t + 8 * (j >> 2) + 4 * hh + (j & 3);
-          bool k_ok = key < x.skv;
-          if (p.band) k_ok = k_ok && (key - row <= p.next) && (row - key <= p.pre);
+          bool k_ok = b0 + (uint32_t)(32 * t + 8 * (j >> 2) + (j & 3)) <= span;
           if (bk.read_mask) k_ok = k_ok && ((mw[4 * t + (j >> 2)] >> (8 * (j & 3))) & 0xffu) == 0;
-          float b0 = 0.f;
+          float bv = 0.f;
           if constexpr (DR == 0) {  // pse and rope do not combine
-            if (p.has_pse) b0 = pse_elem<T>(pw[4 * t + (j >> 2)], j & 3) * p.inv_scale;
+            if (p.has_pse) bv = pse_elem<T>(pw[4 * t + (j >> 2)], j & 3) * p.inv_scale;
           }
-          bias[t][j] = k_ok ? b0 : kNegInf;
+          bias[t][j] = k_ok ? bv : kNegInf;
         }
       }
       sacc[0] = mfma32<T>(a0, qf[0], bias[0]);
