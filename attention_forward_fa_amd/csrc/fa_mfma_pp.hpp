@@ -270,6 +270,15 @@ __device__ __forceinline__ void pp_softmax(const Params& p, const PpCtx<T>& x, i
   const bool edge = p.band && !(jb >= x.g_last - p.pre && jb + BN - 1 <= x.g_first + p.next);
   const bool rmask = mask_class(p, x.cls_row, jb) == CLS_MIXED;
   if (tail || edge || rmask) {
+    // the row keeps keys [lo, hi]; element (t, a, b) is key jb + 4hh + 32t +
+    // 8a + b, kept iff unsigned(b0 + 32t + 8a + b) <= span with b0 = jb + 4hh - lo
+    int lo = 0, hi = x.skv - 1;
+    if (p.band) {
+      lo = max(lo, x.row - p.pre);
+      hi = min(hi, x.row + p.next);
+    }
+    const uint32_t span = hi >= lo ? (uint32_t)(hi - lo) : 0u;
+    const uint32_t b0 = hi >= lo ? (uint32_t)(jb + 4 * x.hh - lo) : 0x80000000u;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -278,9 +287,7 @@ __device__ __forceinline__ void pp_softmax(const Params& p, const PpCtx<T>& x, i
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int j = 4 * a + b;
-          const int key = jb + 32 * t + 8 * a + 4 * x.hh + b;
-          bool k_ok = key < x.skv;
-          if (p.band) k_ok = k_ok && (key - x.row <= p.next) && (x.row - key <= p.pre);
+          bool k_ok = b0 + (uint32_t)(32 * t + 8 * a + b) <= span;
           k_ok = k_ok && ((mword >> (8 * b)) & 0xffu) == 0;
           st.sacc[t][j] = k_ok ? st.sacc[t][j] : kNegInf;
         }
