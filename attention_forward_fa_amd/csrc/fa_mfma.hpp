@@ -405,11 +405,19 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
   }
 
   // ---- online softmax (per lane: one query row, 32 of the block's keys)
-  float mx = kNegInf;
+  float mx;
+  {
+    // two chains of 3-input maxima (v_max3): 16 instructions for 32 values
+    auto max3 = [](float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); };
+    float m0 = max3(sacc[0][0], sacc[0][1], sacc[0][2]);
+    float m1 = max3(sacc[1][0], sacc[1][1], sacc[1][2]);
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) mx = __builtin_fmaxf(mx, sacc[t][j]);
+    for (int j = 3; j < 15; j += 2) {
+      m0 = max3(m0, sacc[0][j], sacc[0][j + 1]);
+      m1 = max3(m1, sacc[1][j], sacc[1][j + 1]);
+    }
+    mx = __builtin_fmaxf(max3(m0, m1, sacc[0][15]), sacc[1][15]);
+  }
   mx = xhalf_max(mx);
   const float mxc = mx * c;  // c > 0, so -inf stays -inf
   m_max = __builtin_fmaxf(m_max, mxc);
@@ -423,14 +431,17 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
   const float m_use = m_ref == kNegInf ? 0.f : m_ref;
 
   V8 pk[2][2];
+  float ls[4];  // four independent partial sums
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const float e = fast_exp2(fmaf(sacc[t][j], c, -m_use));
-      lsum += e;
+      if (t == 0 && j < 4) ls[j] = e;
+      else ls[j & 3] += e;
       pk[t][j >> 3][j & 7] = from_f32<T>(e);
     }
+  lsum += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
   // ---- O^T += V^T P^T.  V^T operand: lane group q = lane / 16 covers output
   // columns 32 dt + 16 (q & 1) + 0..15 and keys kb = 32 t + 16 s2 + 4 (q >> 1)
