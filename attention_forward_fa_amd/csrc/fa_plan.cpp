@@ -346,8 +346,10 @@ extern "C" fa_status fa_fwd_get_workspace_size(
                        (!query_rope || (vec_ok(query_rope->data, qr) && vec_ok(key_rope->data, kr))) && stats_vec;
   // Family: the two-group (ping-pong) matrix-core kernel for long dense
   // sequences at D = 128 without rope whose window cuts at most the causal
-  // side, with at least one workgroup per compute unit (it measures faster
-  // there: one K / V stream serves 256 query rows); the four-wave
+  // side or is at least 2048 keys wide (narrower windows waste a larger share
+  // of the steps, since the two groups' key ranges differ by 128 rows), with
+  // at least one workgroup per compute unit (it measures faster there: one
+  // K / V stream serves 256 query rows); the four-wave
   // matrix-core kernel wherever else it applies (short or varlen sequences,
   // rope, sliding windows, D = 64, grids too small for the two-group kernel,
   // which it may split along the keys); the generic kernel for everything
@@ -355,7 +357,7 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   // benchmarks); forcing a matrix-core family on a shape it does not cover is
   // an error.
   const bool pp_pref = q.d == 128 && dr == 0 && L != L_TND && q.s >= 1024 && k.s >= 1024 &&
-                       (!band || pre >= k.s - 1) && !real_shift &&
+                       (!band || pre >= k.s - 1 || pre + nxt >= 2047) && !real_shift &&
                        q.b * q.n * cdiv(q.s, fa::kMfmaPpBM) >= fa::kNumCUs;
   int kind = mfma_ok ? (pp_pref ? fa::KERNEL_MFMA_PP : fa::KERNEL_MFMA) : fa::KERNEL_GENERIC;
   if (const char* force = getenv("FA_FWD_KERNEL")) {

@@ -357,7 +357,8 @@ def test_describe_truncates_safely():
 
 @pytest.mark.parametrize("case,family", [
     ("causal", "mfma_pp"),      # the window cuts only the causal side
-    ("band", "mfma"),           # sliding window: the four-wave kernel
+    ("band", "mfma"),           # narrow sliding window: the four-wave kernel
+    ("wide_band", "mfma_pp"),   # a window of 2048 + 1 keys: the two-group kernel
     ("rope", "mfma"),
     ("d64", "mfma"),
 ])
@@ -365,8 +366,8 @@ def test_family_policy(case, family):
     S, N = 4096, 16  # 256 two-group workgroups: one per compute unit
     q = desc([1, N, S, 128 if case != "d64" else 64])
     kw = dict(layout=b"BNSD")
-    if case in ("causal", "band"):
-        kw.update(causal=1, pre=(2**31 - 1) if case == "causal" else 1024, nxt=0)
+    if case in ("causal", "band", "wide_band"):
+        kw.update(causal=1, pre={"causal": 2**31 - 1, "band": 1024, "wide_band": 2048}[case], nxt=0)
     if case == "rope":
         r = desc([1, N, S, 64])
         kw.update(qr=r, kr=r)
