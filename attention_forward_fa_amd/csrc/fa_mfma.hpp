@@ -29,6 +29,11 @@
 // the operand reads hit distinct banks.  The V^T operand is read with the
 // transposing LDS load (ds_read_tr16_b64), which hands each lane 4 keys of
 // one column, so V is never transposed explicitly.
+//
+// A dense grid too small to fill the chip may give each query tile up to 4
+// workgroups over disjoint key ranges (kv_splits); each then writes its rows'
+// output over its range, normalised, in fp32 with the range's max and sum,
+// and a second kernel (fa_split_merge_kernel) combines the ranges.
 #pragma once
 
 #include "fa_device.hpp"
