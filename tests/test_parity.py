@@ -270,6 +270,9 @@ SPLIT = {
     "block_mask": lambda: _block_mask_case(108, 128, 64, (1, 2)),
     "window_mask_empty_rows": lambda: _split_window_case(109),
     "sbh_layout": lambda: _split_sbh_case(110),
+    "one_row_short_tail": lambda: synth.dense_case("x", "BNSD", 1, 2, 1, 128, "bf16", 112, skv=70, sink=True),
+    "d64_gqa_band": lambda: synth.dense_case("x", "BSND", 2, 4, 190, 64, "fp16", 113, nkv=1, skv=610, causal=True,
+                                             pre_tokens=200),
 }
 
 
