@@ -73,14 +73,19 @@ struct MfmaCfg {
   static constexpr int NDT = DV / 32;                        // 32-wide output tiles
 };
 
-// Physical 16-byte unit of logical unit u in LDS row r.  K rows: reads of 8
-// consecutive rows at one unit (one ds_read_b128 quarter-wave) land on 8
-// different units.  V rows: the transposing reads touch 4 consecutive rows at
-// an even/odd unit pair; an even XOR keeps the pair contiguous and spreads the
-// 4 rows over distinct banks.
-__device__ __forceinline__ int k_swz(int r, int u) { return u ^ (r & 7); }
+// Physical 16-byte unit of logical unit u in LDS row r (the LDS serves 256
+// bytes, 16 units, per cycle).  K rows: a ds_read_b128 reads one unit of 16
+// consecutive rows per 16 lanes; with 256-byte rows the XOR by r & 15 puts
+// them on 16 different units, with 128-byte rows (two per 256 bytes) the XOR
+// by (r >> 1) & 7 does.  V rows: 32 lanes of the transposing read touch 4
+// consecutive rows at 4 consecutive units (two even/odd pairs); the XOR by
+// (r & 3) << 2 moves each row to its own group of 4 units.  (Measured on the
+// two-group kernel at B2 S4096 N24: LDS bank-conflict cycles fell from about
+// half of the LDS busy cycles to under 1%.)
+template <int U>
+__device__ __forceinline__ int k_swz(int r, int u) { return U >= 16 ? u ^ (r & 15) : u ^ ((r >> 1) & 7); }
 template <int VU>
-__device__ __forceinline__ int v_swz(int r, int u) { return VU >= 16 ? u ^ ((r & 7) << 1) : u ^ ((r & 3) << 1); }
+__device__ __forceinline__ int v_swz(int r, int u) { return VU >= 16 ? u ^ ((r & 3) << 2) : u ^ ((r & 3) << 1); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -179,7 +184,7 @@ __device__ __forceinline__ void stage_block(char* __restrict__ st, int jb, const
 #pragma unroll
   for (int n = 0; n < C::K_LOADS; ++n) {
     const int unit = 64 * (4 * n + x.wave) + x.lane;
-    const int r = unit / C::KU, u = k_swz(r, unit % C::KU);
+    const int r = unit / C::KU, u = k_swz<C::KU>(r, unit % C::KU);
     dma16(kb, rows * x.krow_b, (lds_void*)(st + 1024 * (4 * n + x.wave)), (uint32_t)(r * x.krow_b + u * 16));
   }
   if constexpr (DR > 0) {
@@ -187,7 +192,7 @@ __device__ __forceinline__ void stage_block(char* __restrict__ st, int jb, const
 #pragma unroll
     for (int n = 0; n < C::KR_LOADS; ++n) {
       const int unit = 64 * (4 * n + x.wave) + x.lane;
-      const int r = unit / C::KRU, u = k_swz(r, unit % C::KRU);
+      const int r = unit / C::KRU, u = k_swz<C::KRU>(r, unit % C::KRU);
       dma16(krb, rows * x.krrow_b, (lds_void*)(st + C::KR_OFF + 1024 * (4 * n + x.wave)),
             (uint32_t)(r * x.krrow_b + u * 16));
     }
@@ -335,8 +340,8 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
   // mask words are consumed before the next block's overwrite them.
   auto kfrag = [&](int ks, int t) {
     const int r = 32 * t + l32;
-    const char* src = ks < D / 16 ? cur + (r * C::KU + k_swz(r, 2 * ks + hh)) * 16
-                                  : cur + C::KR_OFF + (r * C::KRU + k_swz(r, 2 * (ks - D / 16) + hh)) * 16;
+    const char* src = ks < D / 16 ? cur + (r * C::KU + k_swz<C::KU>(r, 2 * ks + hh)) * 16
+                                  : cur + C::KR_OFF + (r * C::KRU + k_swz<C::KRU>(r, 2 * (ks - D / 16) + hh)) * 16;
     return *reinterpret_cast<const V8*>(src);
   };
   const BlockKind bk = block_kind(p, jb, x);

@@ -97,13 +97,13 @@ __device__ __forceinline__ void pp_stage_one(char* __restrict__ slot, int jb, co
   if (idx < C::K_LOADS) {
     const T* kb = x.kbase + jbc * (x.krow_b / (int64_t)sizeof(T));
     const int unit = 64 * (8 * idx + x.wave) + x.lane;
-    const int r = unit / C::KU, u = k_swz(r, unit % C::KU);
+    const int r = unit / C::KU, u = k_swz<C::KU>(r, unit % C::KU);
     dma16(kb, rows * x.krow_b, (lds_void*)(slot + 1024 * (8 * idx + x.wave)), (uint32_t)(r * x.krow_b + u * 16));
   } else if (DR > 0 && idx < C::K_LOADS + C::KR_LOADS) {
     const int n = idx - C::K_LOADS;
     const T* krb = x.krbase + jbc * (x.krrow_b / (int64_t)sizeof(T));
     const int unit = 64 * (8 * n + x.wave) + x.lane;
-    const int r = unit / C::KRU, u = k_swz(r, unit % C::KRU);
+    const int r = unit / C::KRU, u = k_swz<C::KRU>(r, unit % C::KRU);
     dma16(krb, rows * x.krrow_b, (lds_void*)(slot + C::KR_OFF + 1024 * (8 * n + x.wave)),
           (uint32_t)(r * x.krrow_b + u * 16));
   } else {
@@ -138,8 +138,8 @@ __device__ __forceinline__ void pp_scores(const char* __restrict__ slot, const P
     for (int t = 0; t < 2; ++t) {
       const int r = 32 * t + x.l32;
       const char* src = kstep < D / 16
-                            ? slot + (r * C::KU + k_swz(r, 2 * kstep + x.hh)) * 16
-                            : slot + C::KR_OFF + (r * C::KRU + k_swz(r, 2 * (kstep - D / 16) + x.hh)) * 16;
+                            ? slot + (r * C::KU + k_swz<C::KU>(r, 2 * kstep + x.hh)) * 16
+                            : slot + C::KR_OFF + (r * C::KRU + k_swz<C::KRU>(r, 2 * (kstep - D / 16) + x.hh)) * 16;
       s[t] = mfma32<T>(*reinterpret_cast<const V8*>(src), qf[kstep], s[t]);
     }
   }
@@ -170,8 +170,8 @@ __device__ __forceinline__ void pp_mphase(const char* __restrict__ kslot, const 
     const int kstep = i >> 1, t = i & 1;
     const int r = 32 * t + x.l32;
     const char* src = kstep < D / 16
-                          ? kslot + (r * C::KU + k_swz(r, 2 * kstep + x.hh)) * 16
-                          : kslot + C::KR_OFF + (r * C::KRU + k_swz(r, 2 * (kstep - D / 16) + x.hh)) * 16;
+                          ? kslot + (r * C::KU + k_swz<C::KU>(r, 2 * kstep + x.hh)) * 16
+                          : kslot + C::KR_OFF + (r * C::KRU + k_swz<C::KRU>(r, 2 * (kstep - D / 16) + x.hh)) * 16;
     return *reinterpret_cast<const V8*>(src);
   };
   // P V MFMA i: output tile dt = i % NDT, key step (t, s2) = i / NDT, so
