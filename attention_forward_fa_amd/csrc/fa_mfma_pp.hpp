@@ -67,6 +67,7 @@ struct PpCtx {
   const T* vbase;
   const T* krbase;
   int64_t krow_b, vrow_b, krrow_b;
+  int kn, krn, vn;  // bytes of the sequence's K, Krope, V rows from its first (reads past them return zeros)
   const uint8_t* mrow;  // this lane's mask row (blocks that read the mask)
   const uint8_t* cls_row;  // this group's mask block classes (null: outside a TND mask)
   int skv, row, g_first, g_last;
@@ -86,33 +87,32 @@ struct PpState {
 
 // All 512 threads, load `idx` of the LPB that stage the K (+ Krope) and V of
 // the block at jb into `slot`: load n of a part, from wave w, fills LDS units
-// [64 (8n + w), +64) of that part; rows past the sequence end (or a block past
-// the last) read as zeros.
+// [64 (8n + w), +64) of that part.  One buffer descriptor per tensor covers
+// the sequence's rows (bytes kn / krn / vn from its first row); the block
+// enters only the lane's 32-bit byte offset (planning keeps those offsets, up
+// to (Skv + 4 blocks) rows, under 2^31), and rows past the sequence end (or a
+// block past the last) fall outside the descriptor and read as zeros.
 template <typename T, int D, int DR>
 __device__ __forceinline__ void pp_stage_one(char* __restrict__ slot, int jb, const PpCtx<T>& x, int idx) {
   using C = PpCfg<T, D, DR>;
-  jb = __builtin_amdgcn_readfirstlane(jb);  // uniform: the descriptors stay scalar
-  const int64_t rows = max(min(x.skv - jb, C::BN), 0);
-  const int64_t jbc = min(jb, x.skv);  // keeps the base inside the tensor
+  jb = __builtin_amdgcn_readfirstlane(jb);  // uniform
   if (idx < C::K_LOADS) {
-    const T* kb = x.kbase + jbc * (x.krow_b / (int64_t)sizeof(T));
     const int unit = 64 * (8 * idx + x.wave) + x.lane;
     const int r = unit / C::KU, u = k_swz<C::KU>(r, unit % C::KU);
-    dma16(kb, rows * x.krow_b, (lds_void*)(slot + 1024 * (8 * idx + x.wave)), (uint32_t)(r * x.krow_b + u * 16));
+    dma16(x.kbase, x.kn, (lds_void*)(slot + 1024 * (8 * idx + x.wave)),
+          (uint32_t)(jb + r) * (uint32_t)x.krow_b + u * 16);
   } else if (DR > 0 && idx < C::K_LOADS + C::KR_LOADS) {
     const int n = idx - C::K_LOADS;
-    const T* krb = x.krbase + jbc * (x.krrow_b / (int64_t)sizeof(T));
     const int unit = 64 * (8 * n + x.wave) + x.lane;
     const int r = unit / C::KRU, u = k_swz<C::KRU>(r, unit % C::KRU);
-    dma16(krb, rows * x.krrow_b, (lds_void*)(slot + C::KR_OFF + 1024 * (8 * n + x.wave)),
-          (uint32_t)(r * x.krrow_b + u * 16));
+    dma16(x.krbase, x.krn, (lds_void*)(slot + C::KR_OFF + 1024 * (8 * n + x.wave)),
+          (uint32_t)(jb + r) * (uint32_t)x.krrow_b + u * 16);
   } else {
     const int n = idx - C::K_LOADS - C::KR_LOADS;
-    const T* vb = x.vbase + jbc * (x.vrow_b / (int64_t)sizeof(T));
     const int unit = 64 * (8 * n + x.wave) + x.lane;
     const int r = unit / C::VU, u = v_swz<C::VU>(r, unit % C::VU);
-    dma16(vb, rows * x.vrow_b, (lds_void*)(slot + C::V_OFF + 1024 * (8 * n + x.wave)),
-          (uint32_t)(r * x.vrow_b + u * 16));
+    dma16(x.vbase, x.vn, (lds_void*)(slot + C::V_OFF + 1024 * (8 * n + x.wave)),
+          (uint32_t)(jb + r) * (uint32_t)x.vrow_b + u * 16);
   }
 }
 
@@ -443,6 +443,15 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
   x.krow_b = p.k_ss * (int64_t)sizeof(T);
   x.vrow_b = p.v_ss * (int64_t)sizeof(T);
   x.krrow_b = DR ? p.kr_ss * (int64_t)sizeof(T) : 0;
+  {
+    auto nbytes = [&](int64_t row_b) {
+      const int64_t nb = (int64_t)tl.skv * row_b;
+      return (int)(nb < 0x7fffffff ? nb : 0x7fffffff);
+    };
+    x.kn = nbytes(x.krow_b);
+    x.vn = nbytes(x.vrow_b);
+    x.krn = DR ? nbytes(x.krrow_b) : 0;
+  }
   x.mrow = nullptr;
   if (p.has_mask) {  // dense: [b|0, h|0, row, :]; TND: the 2-D mask in local coordinates
     if (p.varlen)

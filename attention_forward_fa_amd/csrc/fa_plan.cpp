@@ -356,7 +356,13 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   // else.  FA_FWD_KERNEL=mfma|pp|generic forces a family (tests and
   // benchmarks); forcing a matrix-core family on a shape it does not cover is
   // an error.
-  const bool pp_pref = q.d == 128 && dr == 0 && L != L_TND && q.s >= 1024 && k.s >= 1024 &&
+  // the two-group kernel addresses a sequence's K / V rows with 32-bit byte
+  // offsets from its first row, up to Skv + 4 blocks of rows
+  const int64_t esz = dt == FA_DTYPE_F32 ? 4 : 2;
+  int64_t row_b = k.ss > v.ss ? k.ss : v.ss;
+  if (query_rope && kr.ss > row_b) row_b = kr.ss;
+  const bool pp_fits = (k.s + 4 * fa::kMfmaBN) * row_b * esz < ((int64_t)1 << 31);
+  const bool pp_pref = pp_fits && q.d == 128 && dr == 0 && L != L_TND && q.s >= 1024 && k.s >= 1024 &&
                        (!band || pre >= k.s - 1 || pre + nxt >= 2047) && !real_shift &&
                        q.b * q.n * cdiv(q.s, fa::kMfmaPpBM) >= fa::kNumCUs;
   int kind = mfma_ok ? (pp_pref ? fa::KERNEL_MFMA_PP : fa::KERNEL_MFMA) : fa::KERNEL_GENERIC;
@@ -371,6 +377,10 @@ extern "C" fa_status fa_fwd_get_workspace_size(
       if (!strcmp(force, "pp") && real_shift) {
         delete pl;
         return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL=pp: the two-group kernel takes no real_shift");
+      }
+      if (!strcmp(force, "pp") && !pp_fits) {
+        delete pl;
+        return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL=pp: K / V rows of one sequence span 2 GiB or more");
       }
       kind = !strcmp(force, "pp") ? fa::KERNEL_MFMA_PP : fa::KERNEL_MFMA;
     } else if (force[0] != '\0') {

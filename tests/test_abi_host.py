@@ -442,6 +442,23 @@ def test_key_split_limits(monkeypatch):
         assert st == 561103 and pl is None and "FA_FWD_KV_SPLIT" in _lib.last_error_message()
 
 
+def test_two_group_kernel_needs_32bit_row_offsets(monkeypatch):
+    # BSND N128 D128: 32 KiB per key row; 65536 keys (+ 4 blocks) span 2 GiB, past the two-group kernel's
+    # 32-bit offsets, so the four-wave kernel takes the call (and forcing the two-group one is refused)
+    s = [1, 65536, 128, 128]
+    st, ws, pl = plan(desc(s), desc(s), desc(s), desc(s))
+    assert st == 0, _lib.last_error_message()
+    assert "kernel=mfma " in describe(pl), describe(pl)
+    _lib.fa_plan_destroy(pl)
+    s2 = [1, 65536 - 8192, 128, 128]  # (57344 + 256) rows x 32 KiB < 2 GiB
+    st, ws, pl = plan(desc(s2), desc(s2), desc(s2), desc(s2))
+    assert st == 0 and "kernel=mfma_pp " in describe(pl), describe(pl)
+    _lib.fa_plan_destroy(pl)
+    monkeypatch.setenv("FA_FWD_KERNEL", "pp")
+    st, _, pl = plan(desc(s), desc(s), desc(s), desc(s))
+    assert st == 561103 and pl is None and "2 GiB" in _lib.last_error_message()
+
+
 def test_small_grid_uses_four_wave_kernel():
     s = [1, 300, 2, 128]
     st, ws, pl = plan(desc(s), desc(s), desc(s), desc(s))
