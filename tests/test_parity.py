@@ -368,6 +368,19 @@ def test_bitwise_deterministic(name, kernel):
                            y.view(torch.uint8) if y.dtype != torch.float32 else y.view(torch.int32))
 
 
+@pytest.mark.parametrize("splits", ["2", "4"])
+def test_key_split_bitwise_deterministic(splits, monkeypatch):
+    """The split's partials and merge use no atomics: two runs agree bit for bit."""
+    monkeypatch.setenv("FA_FWD_KV_SPLIT", splits)
+    case = SPLIT["d128_rope_sink"]()
+    with pu.forced_kernel("mfma"):
+        a = pu.run_gpu(case)
+        b = pu.run_gpu(case)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype != torch.float32 else x.view(torch.int32),
+                           y.view(torch.uint8) if y.dtype != torch.float32 else y.view(torch.int32))
+
+
 def test_guard_bands_untouched():
     case = synth.workload("c4_varlen_causal", small=True)
     T, N, D = case.q.shape
@@ -386,6 +399,33 @@ def test_guard_bands_untouched():
     for buf in (obuf, sbuf):
         assert bool((buf[:pad] == poison).all()) and bool((buf[-pad:] == poison).all())
     assert not bool((out == poison).any())
+    O, M, _ = pu.run_oracle(case)
+    pu.check_output(out.cpu(), O, torch.bfloat16)
+    pu.check_stats(smax.cpu(), M, "max", torch.bfloat16)
+    plan.close()
+
+
+def test_key_split_guard_bands_untouched(monkeypatch):
+    """The split writes only its workspace and, through the merge, exactly the output and statistics rows."""
+    monkeypatch.setenv("FA_FWD_KV_SPLIT", "3")
+    case = SPLIT["dense_ragged"]()  # BNSD [2, 3, 201, 128], 650 keys
+    B, N, S, D = case.q.shape
+    pad = 4096
+    poison = -12345.0
+    obuf = torch.full((pad + B * N * S * D + pad,), poison, dtype=torch.bfloat16, device="cuda")
+    out = obuf[pad:pad + B * N * S * D].view(B, N, S, D)
+    sbuf = torch.full((pad + B * N * S * 8 + pad,), poison, dtype=torch.float32, device="cuda")
+    smax = sbuf[pad:pad + B * N * S * 8].view(B, N, S, 8)
+    g = {k: pu.to_gpu(v) for k, v in case.tensors().items()}
+    with pu.forced_kernel("mfma"):
+        plan = api.ForwardPlan(g["q"], g["k"], g["v"], layout="BNSD", scale=case.scale, head_num=N, out=out,
+                               softmax_max=smax, softmax_sum=None)
+    assert "kv_splits=3" in plan.describe(), plan.describe()
+    plan.run()
+    torch.cuda.synchronize()
+    for buf in (obuf, sbuf):
+        assert bool((buf[:pad] == poison).all()) and bool((buf[-pad:] == poison).all())
+    assert not bool((out == poison).any()) and not bool((smax == poison).any())
     O, M, _ = pu.run_oracle(case)
     pu.check_output(out.cpu(), O, torch.bfloat16)
     pu.check_stats(smax.cpu(), M, "max", torch.bfloat16)
