@@ -167,8 +167,9 @@ typedef int32_t fa_status;
  * Dr is 0 or 64, Dv == D and every row start is 16-byte aligned (the
  * two-group one for dense Sq, Skv >= 1024 at D = 128 without rope or pse
  * whose window cuts at most the causal side or spans at least 2048 keys
- * (pre + next >= 2047) and whose grid of 256-row tiles has at least 256
- * workgroups, else the four-wave one);
+ * (pre + next >= 2047), whose grid of 256-row tiles has at least 256
+ * workgroups and whose K / V rows of one sequence span under 2 GiB, else the
+ * four-wave one);
  * otherwise the generic one (fp32 dot products on the vector units).  The environment
  * variable FA_FWD_KERNEL = "mfma" | "pp" | "generic", read here, forces a
  * family for testing; forcing one the arguments do not fit returns
