@@ -34,7 +34,7 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 HBM_GBPS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCES = ["fa_mfma.hpp", "fa_mfma_pp.hpp", "fa_device.hpp", "fa_params.h", "fa_mfma_bf16.hip",
-                  "fa_mfma_f16.hip", "fa_generic.hip", "fa_launch.hip"]
+                  "fa_mfma_f16.hip", "fa_generic.hip", "fa_launch.hip", "fa_merge.hip"]
 
 
 def kernel_source_hash() -> str:
