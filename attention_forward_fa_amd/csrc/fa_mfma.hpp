@@ -82,10 +82,16 @@ struct MfmaCfg {
 // (r & 3) << 2 moves each row to its own group of 4 units.  (Measured on the
 // two-group kernel at B2 S4096 N24: LDS bank-conflict cycles fell from about
 // half of the LDS busy cycles to under 1%.)
+// Rows of 12 units (D = 96) are not swizzled: their 192-byte stride already
+// staggers consecutive rows over the banks, and no XOR stays inside 12 units.
 template <int U>
-__device__ __forceinline__ int k_swz(int r, int u) { return U >= 16 ? u ^ (r & 15) : u ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int k_swz(int r, int u) {
+  return U % 16 == 0 ? u ^ (r & 15) : (U == 8 ? u ^ ((r >> 1) & 7) : u);
+}
 template <int VU>
-__device__ __forceinline__ int v_swz(int r, int u) { return VU >= 16 ? u ^ ((r & 3) << 2) : u ^ ((r & 3) << 1); }
+__device__ __forceinline__ int v_swz(int r, int u) {
+  return VU % 16 == 0 ? u ^ ((r & 3) << 2) : (VU == 8 ? u ^ ((r & 3) << 1) : u);
+}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -119,6 +125,10 @@ constexpr float kLazy = 8.0f;
 // with 16-byte writes, so each row leaves as one contiguous run.  Rows at or
 // past nrows are not written.  Every thread of the workgroup must call it;
 // the LDS must no longer be in use (no loads in flight into it).
+template <int U>
+__device__ __forceinline__ int o_swz(int r, int u) {  // a permutation of [0, U) per row
+  return (U & (U - 1)) == 0 ? u ^ (r % U) : (u + r) % U;
+}
 template <typename T, int DV, int NTHREADS>
 __device__ __forceinline__ void o_tile_store(char* __restrict__ lds, const f32x16 (&oacc)[DV / 32], float inv,
                                              int lrow, int hh, T* __restrict__ obase, int64_t o_ss, int nrows) {
@@ -130,14 +140,14 @@ __device__ __forceinline__ void o_tile_store(char* __restrict__ lds, const f32x1
       T v4[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v4[e] = from_f32<T>(oacc[dt][4 * g4 + e] * inv);
-      const int pu = (4 * dt + g4) ^ (lrow % U);
+      const int pu = o_swz<U>(lrow, 4 * dt + g4);
       *reinterpret_cast<uint2*>(lds + (lrow * U + pu) * 16 + 8 * hh) = *reinterpret_cast<const uint2*>(v4);
     }
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < nrows * U; idx += NTHREADS) {
     const int r = idx / U, u = idx - r * U;
-    const uint4 v = *reinterpret_cast<const uint4*>(lds + (r * U + (u ^ (r % U))) * 16);
+    const uint4 v = *reinterpret_cast<const uint4*>(lds + (r * U + o_swz<U>(r, u)) * 16);
     *reinterpret_cast<uint4*>(obase + r * o_ss + 8 * u) = v;
   }
 }

@@ -38,6 +38,12 @@ static hipError_t launch_mfma_t(const Params& p, hipStream_t s) {
     fn = reinterpret_cast<const void*>(&fa_fwd_mfma<T, 64, 0>);
   else if (p.d == 64 && p.dr == 64)
     fn = reinterpret_cast<const void*>(&fa_fwd_mfma<T, 64, 64>);
+  else if (p.pse_lds && p.d == 96 && p.dr == 0)
+    fn = reinterpret_cast<const void*>(&fa_fwd_mfma<T, 96, 0, true>);
+  else if (p.d == 96 && p.dr == 0)
+    fn = reinterpret_cast<const void*>(&fa_fwd_mfma<T, 96, 0>);
+  else if (p.d == 96 && p.dr == 64)
+    fn = reinterpret_cast<const void*>(&fa_fwd_mfma<T, 96, 64>);
   else
     return hipErrorInvalidValue;
   return hipLaunchKernel(fn, dim3(p.num_wg), dim3(kMfmaThreads), args, 0, s);

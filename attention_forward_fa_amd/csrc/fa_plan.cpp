@@ -340,7 +340,7 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   pl->dtype = dt;
   const bool stats_vec = (!softmax_max || aligned16(softmax_max->data)) && (!softmax_sum || aligned16(softmax_sum->data)) &&
                          st_sb % 4 == 0 && st_ss % 4 == 0 && st_sh % 4 == 0;
-  const bool mfma_ok = (dt == FA_DTYPE_F16 || dt == FA_DTYPE_BF16) && (q.d == 64 || q.d == 128) && v.d == q.d &&
+  const bool mfma_ok = (dt == FA_DTYPE_F16 || dt == FA_DTYPE_BF16) && (q.d == 64 || q.d == 96 || q.d == 128) && v.d == q.d &&
                        (dr == 0 || dr == 64) && vec_ok(query->data, q) && vec_ok(key->data, k) &&
                        vec_ok(value->data, v) && vec_ok(attention_out->data, o) &&
                        (!query_rope || (vec_ok(query_rope->data, qr) && vec_ok(key_rope->data, kr))) && stats_vec;
@@ -377,6 +377,10 @@ extern "C" fa_status fa_fwd_get_workspace_size(
       if (!strcmp(force, "pp") && real_shift) {
         delete pl;
         return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL=pp: the two-group kernel takes no real_shift");
+      }
+      if (!strcmp(force, "pp") && q.d == 96) {
+        delete pl;
+        return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL=pp: the two-group kernel has D = 64 and 128 only");
       }
       if (!strcmp(force, "pp") && !pp_fits) {
         delete pl;

@@ -163,7 +163,7 @@ typedef int32_t fa_status;
  *                       fa_plan_destroy().  It records the tensors' device
  *                       addresses; it may be executed any number of times.
  *
- * Kernel choice: a matrix-core kernel when q is F16/BF16, D is 64 or 128,
+ * Kernel choice: a matrix-core kernel when q is F16/BF16, D is 64, 96 or 128,
  * Dr is 0 or 64, Dv == D and every row start is 16-byte aligned (the
  * two-group one for dense Sq, Skv >= 1024 at D = 128 without rope or pse
  * whose window cuts at most the causal side or spans at least 2048 keys

@@ -459,6 +459,20 @@ def test_two_group_kernel_needs_32bit_row_offsets(monkeypatch):
     assert st == 561103 and pl is None and "2 GiB" in _lib.last_error_message()
 
 
+@pytest.mark.parametrize("dr", [0, 64])
+def test_d96_on_matrix_cores(dr, monkeypatch):
+    s = [2, 1024, 8, 96]
+    kw = dict(qr=desc([2, 1024, 8, 64]), kr=desc([2, 1024, 8, 64])) if dr else {}
+    st, ws, pl = plan(desc(s), desc(s), desc(s), desc(s), **kw)
+    assert st == 0, _lib.last_error_message()
+    d = describe(pl)
+    assert "kernel=mfma " in d and "d=96 " in d and f"dr={dr} " in d, d
+    _lib.fa_plan_destroy(pl)
+    monkeypatch.setenv("FA_FWD_KERNEL", "pp")  # the two-group kernel has no D = 96
+    st, _, pl = plan(desc(s), desc(s), desc(s), desc(s), **kw)
+    assert st == 561103 and pl is None and "D = 64 and 128" in _lib.last_error_message()
+
+
 def test_small_grid_uses_four_wave_kernel():
     s = [1, 300, 2, 128]
     st, ws, pl = plan(desc(s), desc(s), desc(s), desc(s))

@@ -63,7 +63,14 @@ SMALL = {
     "fp32_varlen_sink": lambda: synth.varlen_case("x", [33, 0, 90], 2, 64, "fp32", 46, sink=True, causal=True),
     "fp32_mask_band": lambda: _band_mask_case(47, 9, 0, dtype="fp32", d=64),
     "fp32_d96": lambda: synth.dense_case("x", "BSND", 1, 2, 75, 96, "fp32", 48, dv=80),
-    "bf16_d96_generic": lambda: synth.dense_case("x", "BNSD", 1, 2, 99, 96, "bf16", 49),
+    "bf16_d96": lambda: synth.dense_case("x", "BNSD", 1, 2, 99, 96, "bf16", 49),
+    "d96_causal_sink_bsnd": lambda: synth.dense_case("x", "BSND", 2, 3, 300, 96, "bf16", 58, sink=True, causal=True,
+                                                     skv=333),
+    "d96_fp16_band_mask": lambda: _band_mask_case(59, 17, 5, dtype="fp16", d=96),
+    "d96_rope_varlen": lambda: synth.varlen_case("x", [150, 0, 61, 200], 2, 96, "bf16", 60, drope=64, sink=True,
+                                                 causal=True),
+    "d96_pse_lds": lambda: synth.dense_case("x", "BNSD", 1, 2, 200, 96, "bf16", 61, skv=264, pse="full",
+                                            causal=True),
     "bf16_dv_lt_d_generic": lambda: synth.dense_case("x", "BNSD", 1, 2, 99, 128, "bf16", 50, dv=64),
     "tnd_mask_2d": lambda: _tnd_mask_case(51),
     "scale_zero": lambda: synth.dense_case("x", "BNSD", 1, 1, 130, 128, "bf16", 52, causal=True, scale=0.0),
@@ -271,6 +278,8 @@ SPLIT = {
     "window_mask_empty_rows": lambda: _split_window_case(109),
     "sbh_layout": lambda: _split_sbh_case(110),
     "one_row_short_tail": lambda: synth.dense_case("x", "BNSD", 1, 2, 1, 128, "bf16", 112, skv=70, sink=True),
+    "d96_sink_causal": lambda: synth.dense_case("x", "BNSD", 1, 3, 180, 96, "bf16", 114, skv=700, sink=True,
+                                                causal=True),
     "d64_gqa_band": lambda: synth.dense_case("x", "BSND", 2, 4, 190, 64, "fp16", 113, nkv=1, skv=610, causal=True,
                                              pre_tokens=200),
 }
