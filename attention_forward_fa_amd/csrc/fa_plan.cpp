@@ -340,8 +340,15 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   pl->dtype = dt;
   const bool stats_vec = (!softmax_max || aligned16(softmax_max->data)) && (!softmax_sum || aligned16(softmax_sum->data)) &&
                          st_sb % 4 == 0 && st_ss % 4 == 0 && st_sh % 4 == 0;
-  const bool mfma_ok = (dt == FA_DTYPE_F16 || dt == FA_DTYPE_BF16) && (q.d == 64 || q.d == 96 || q.d == 128) && v.d == q.d &&
-                       (dr == 0 || dr == 64) && vec_ok(query->data, q) && vec_ok(key->data, k) &&
+  // Dqk = Dv + 64 without rope inputs or pse: on the matrix cores the last 64
+  // dims of q and k serve as the rope part (the same rows and strides), so the
+  // kernels see D = Dv and Dr = 64.
+  const bool tail_split = !query_rope && !real_shift && (dt == FA_DTYPE_F16 || dt == FA_DTYPE_BF16) &&
+                          q.d == v.d + 64 && (v.d == 64 || v.d == 96 || v.d == 128);
+  const int64_t dmain = tail_split ? v.d : q.d;
+  const int64_t drm = tail_split ? 64 : dr;
+  const bool mfma_ok = (dt == FA_DTYPE_F16 || dt == FA_DTYPE_BF16) && (dmain == 64 || dmain == 96 || dmain == 128) &&
+                       v.d == dmain && (drm == 0 || drm == 64) && vec_ok(query->data, q) && vec_ok(key->data, k) &&
                        vec_ok(value->data, v) && vec_ok(attention_out->data, o) &&
                        (!query_rope || (vec_ok(query_rope->data, qr) && vec_ok(key_rope->data, kr))) && stats_vec;
   // Family: the two-group (ping-pong) matrix-core kernel for long dense
@@ -362,7 +369,7 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   int64_t row_b = k.ss > v.ss ? k.ss : v.ss;
   if (query_rope && kr.ss > row_b) row_b = kr.ss;
   const bool pp_fits = (k.s + 4 * fa::kMfmaBN) * row_b * esz < ((int64_t)1 << 31);
-  const bool pp_pref = pp_fits && q.d == 128 && dr == 0 && L != L_TND && q.s >= 1024 && k.s >= 1024 &&
+  const bool pp_pref = pp_fits && dmain == 128 && drm == 0 && L != L_TND && q.s >= 1024 && k.s >= 1024 &&
                        (!band || pre >= k.s - 1 || pre + nxt >= 2047) && !real_shift &&
                        q.b * q.n * cdiv(q.s, fa::kMfmaPpBM) >= fa::kNumCUs;
   int kind = mfma_ok ? (pp_pref ? fa::KERNEL_MFMA_PP : fa::KERNEL_MFMA) : fa::KERNEL_GENERIC;
@@ -378,7 +385,7 @@ extern "C" fa_status fa_fwd_get_workspace_size(
         delete pl;
         return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL=pp: the two-group kernel takes no real_shift");
       }
-      if (!strcmp(force, "pp") && q.d == 96) {
+      if (!strcmp(force, "pp") && dmain == 96) {
         delete pl;
         return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL=pp: the two-group kernel has D = 64 and 128 only");
       }
@@ -401,6 +408,14 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   p.q = query->data; p.k = key->data; p.v = value->data;
   p.qr = query_rope ? query_rope->data : nullptr;
   p.kr = key_rope ? key_rope->data : nullptr;
+  const bool tail_rope = tail_split && kind != fa::KERNEL_GENERIC;  // the generic kernel takes Dv < D as it is
+  if (tail_rope) {
+    const int64_t esz = dt == FA_DTYPE_F32 ? 4 : 2;
+    p.qr = static_cast<const char*>(query->data) + v.d * esz;
+    p.kr = static_cast<const char*>(key->data) + v.d * esz;
+    qr = q;
+    kr = k;
+  }
   p.o = attention_out->data;
   p.smax = softmax_max ? static_cast<float*>(softmax_max->data) : nullptr;
   p.ssum = softmax_sum ? static_cast<float*>(softmax_sum->data) : nullptr;
@@ -459,8 +474,8 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   p.skv = p.varlen ? 0 : (int32_t)k.s;
   p.tq = p.varlen ? (int32_t)q.s : 0;
   p.tkv = p.varlen ? (int32_t)k.s : 0;
-  p.d = (int32_t)q.d;
-  p.dr = (int32_t)dr;
+  p.d = (int32_t)(tail_rope ? dmain : q.d);
+  p.dr = (int32_t)(tail_rope ? drm : dr);
   p.dv = (int32_t)v.d;
   p.scale = (float)scale_value;
   // The kernels turn excluded scores into -inf and rely on -inf * c = -inf;

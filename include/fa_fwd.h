@@ -164,7 +164,9 @@ typedef int32_t fa_status;
  *                       addresses; it may be executed any number of times.
  *
  * Kernel choice: a matrix-core kernel when q is F16/BF16, D is 64, 96 or 128,
- * Dr is 0 or 64, Dv == D and every row start is 16-byte aligned (the
+ * Dr is 0 or 64, Dv == D (or, with no rope inputs and no real_shift,
+ * D == Dv + 64, the last 64 dims of q and k then taking the rope part's
+ * role) and every row start is 16-byte aligned (the
  * two-group one for dense Sq, Skv >= 1024 at D = 128 without rope or pse
  * whose window cuts at most the causal side or spans at least 2048 keys
  * (pre + next >= 2047), whose grid of 256-row tiles has at least 256

@@ -473,6 +473,21 @@ def test_d96_on_matrix_cores(dr, monkeypatch):
     assert st == 561103 and pl is None and "D = 64 and 128" in _lib.last_error_message()
 
 
+@pytest.mark.parametrize("dqk,dv,want", [(192, 128, "d=128 dr=64"), (128, 64, "d=64 dr=64"), (160, 96, "d=96 dr=64")])
+def test_dqk_above_dv_on_matrix_cores(dqk, dv, want):
+    # no rope inputs: the last 64 dims of q and k become the rope part of the matrix-core kernels
+    q, v = desc([1, 512, 4, dqk]), desc([1, 512, 4, dv])
+    st, ws, pl = plan(q, q, v, v)
+    assert st == 0, _lib.last_error_message()
+    d = describe(pl)
+    assert "kernel=mfma " in d and want in d and f"dv={dv} " in d, d
+    _lib.fa_plan_destroy(pl)
+    # with pse (which the rope kernels do not take) or fp32, the generic kernel takes Dv < D as it is
+    st, ws, pl = plan(q, q, v, v, pse=desc([1, 4, 512, 512]), layout=b"BSND")
+    assert st == 0 and "kernel=generic" in describe(pl) and f"d={dqk} dr=0" in describe(pl), describe(pl)
+    _lib.fa_plan_destroy(pl)
+
+
 def test_small_grid_uses_four_wave_kernel():
     s = [1, 300, 2, 128]
     st, ws, pl = plan(desc(s), desc(s), desc(s), desc(s))

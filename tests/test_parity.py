@@ -71,7 +71,11 @@ SMALL = {
                                                  causal=True),
     "d96_pse_lds": lambda: synth.dense_case("x", "BNSD", 1, 2, 200, 96, "bf16", 61, skv=264, pse="full",
                                             causal=True),
-    "bf16_dv_lt_d_generic": lambda: synth.dense_case("x", "BNSD", 1, 2, 99, 128, "bf16", 50, dv=64),
+    "bf16_dv_lt_d": lambda: synth.dense_case("x", "BNSD", 1, 2, 99, 128, "bf16", 50, dv=64),
+    "d192_dv128_causal_sink": lambda: synth.dense_case("x", "BSND", 2, 3, 260, 192, "bf16", 62, dv=128, causal=True,
+                                                       sink=True),
+    "d160_dv96_gqa_fp16": lambda: synth.dense_case("x", "BNSD", 1, 4, 200, 160, "fp16", 63, dv=96, nkv=2, skv=333),
+    "d192_dv128_varlen": lambda: synth.varlen_case("x", [130, 0, 257, 64], 2, 192, "bf16", 64, dv=128, causal=True),
     "tnd_mask_2d": lambda: _tnd_mask_case(51),
     "scale_zero": lambda: synth.dense_case("x", "BNSD", 1, 1, 130, 128, "bf16", 52, causal=True, scale=0.0),
     "stats_same_as_input": lambda: synth.varlen_case("x", [64, 200], 2, 128, "bf16", 53, causal=True,
