@@ -284,6 +284,8 @@ SPLIT = {
     "one_row_short_tail": lambda: synth.dense_case("x", "BNSD", 1, 2, 1, 128, "bf16", 112, skv=70, sink=True),
     "d96_sink_causal": lambda: synth.dense_case("x", "BNSD", 1, 3, 180, 96, "bf16", 114, skv=700, sink=True,
                                                 causal=True),
+    "d192_dv128_tail_rope": lambda: synth.dense_case("x", "BSND", 1, 2, 150, 192, "bf16", 115, dv=128, skv=700,
+                                                     sink=True),
     "d64_gqa_band": lambda: synth.dense_case("x", "BSND", 2, 4, 190, 64, "fp16", 113, nkv=1, skv=610, causal=True,
                                              pre_tokens=200),
 }
