@@ -347,10 +347,19 @@ extern "C" fa_status fa_fwd_get_workspace_size(
                           q.d == v.d + 64 && (v.d == 64 || v.d == 96 || v.d == 128);
   const int64_t dmain = tail_split ? v.d : q.d;
   const int64_t drm = tail_split ? 64 : dr;
-  const bool mfma_ok = (dt == FA_DTYPE_F16 || dt == FA_DTYPE_BF16) && (dmain == 64 || dmain == 96 || dmain == 128) &&
-                       v.d == dmain && (drm == 0 || drm == 64) && vec_ok(query->data, q) && vec_ok(key->data, k) &&
-                       vec_ok(value->data, v) && vec_ok(attention_out->data, o) &&
-                       (!query_rope || (vec_ok(query_rope->data, qr) && vec_ok(key_rope->data, kr))) && stats_vec;
+  // The four-wave kernel stages a key block with 32-bit byte offsets from
+  // the block's first row: row r < 64 of K, V (and Krope) at r * row bytes
+  // must stay below 2^31 (a strided view or an SBH layout can have rows far
+  // apart).
+  const int64_t esz_in = dt == FA_DTYPE_F32 ? 4 : 2;
+  int64_t max_row_b = (k.ss > v.ss ? k.ss : v.ss) * esz_in;
+  if (query_rope && kr.ss * esz_in > max_row_b) max_row_b = kr.ss * esz_in;
+  const bool block_offsets_fit = (int64_t)fa::kMfmaBN * max_row_b < ((int64_t)1 << 31);
+  const bool mfma_shape = (dt == FA_DTYPE_F16 || dt == FA_DTYPE_BF16) && (dmain == 64 || dmain == 96 || dmain == 128) &&
+                          v.d == dmain && (drm == 0 || drm == 64) && vec_ok(query->data, q) && vec_ok(key->data, k) &&
+                          vec_ok(value->data, v) && vec_ok(attention_out->data, o) &&
+                          (!query_rope || (vec_ok(query_rope->data, qr) && vec_ok(key_rope->data, kr))) && stats_vec;
+  const bool mfma_ok = mfma_shape && block_offsets_fit;
   // Family: the two-group (ping-pong) matrix-core kernel for long dense
   // sequences at D = 128 without rope whose window cuts at most the causal
   // side or is at least 2048 keys wide (narrower windows waste a larger share
@@ -377,6 +386,11 @@ extern "C" fa_status fa_fwd_get_workspace_size(
     if (!strcmp(force, "generic")) {
       kind = fa::KERNEL_GENERIC;
     } else if (!strcmp(force, "mfma") || !strcmp(force, "pp")) {
+      if (mfma_shape && !block_offsets_fit) {
+        delete pl;
+        return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL=%s: 64 key rows span 2 GiB or more (32-bit block offsets)",
+                    force);
+      }
       if (!mfma_ok) {
         delete pl;
         return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL=%s: shape, dtype or alignment not covered", force);
@@ -497,8 +511,11 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   p.reverse_tiles = band && nxt < max_keys - 1;
   p.pse_vec4 = p.has_pse && !p.varlen && (reinterpret_cast<uintptr_t>(p.pse) & 7u) == 0 && p.ps_sq % 4 == 0 &&
                p.ps_sb % 4 == 0 && p.ps_sh % 4 == 0;
+  // pse through LDS reads the 128 x 64 tile with 32-bit byte offsets from
+  // its first element: row r < 128 at r * row bytes must stay below 2^31
   p.pse_lds = p.has_pse && !p.varlen && dr == 0 && (reinterpret_cast<uintptr_t>(p.pse) & 15u) == 0 &&
-              p.ps_sq % 8 == 0 && p.ps_sb % 8 == 0 && p.ps_sh % 8 == 0 && p.ps_sq < ((int64_t)1 << 24);
+              p.ps_sq % 8 == 0 && p.ps_sb % 8 == 0 && p.ps_sh % 8 == 0 &&
+              (int64_t)fa::kMfmaBM * p.ps_sq * esz_in < ((int64_t)1 << 31);
 
   const int64_t bm = pl->bm;
   int64_t tiles, wg;

@@ -36,7 +36,8 @@ reason in the design notes):
     sequence and a query never sees another sequence's keys (V5 约束说明 on
     TND: T is B and S packed tightly).  A mask given with TND is one 2-D
     [S1, S2] matrix read in sequence-local coordinates (the V5 call example
-    passes a [256, 256] mask with TND).
+    passes a [256, 256] mask with TND); a position of a sequence that lies
+    beyond the mask's rows or columns counts as excluded.
   * The sink is in logit units: it is neither scaled nor biased.  A sink of
     -inf contributes nothing (it must equal "no sink").
   * A row with no kept key has O = 0, m = -inf, l = 0 without a sink, and
@@ -261,6 +262,20 @@ def attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, layo
     return from_bnsd(O, layout), M, L
 
 
+def _tnd_mask(atten_mask: torch.Tensor, lq: int, lk: int) -> torch.Tensor:
+    """The 2-D TND mask as seen by one sequence of lq rows and lk keys.
+
+    Sequence-local position (i, j) reads atten_mask[i, j]; where the sequence
+    is longer than the mask in either direction, the positions outside it are
+    excluded (the reading of the V5 parameter table, row attenMaskOptional,
+    for a [S1, S2] mask smaller than a sequence).
+    """
+    out = torch.ones(lq, lk, dtype=atten_mask.dtype)
+    r, c = min(lq, atten_mask.shape[0]), min(lk, atten_mask.shape[1])
+    out[:r, :c] = atten_mask[:r, :c]
+    return out
+
+
 def _as_list(cu) -> list:
     return [int(x) for x in (cu.tolist() if isinstance(cu, torch.Tensor) else cu)]
 
@@ -294,7 +309,7 @@ def _forward_tnd(q, k, v, *, scale, q_rope, k_rope, atten_mask, sink, causal, pr
         return head_attention(q[q0:q1, h], k[k0:k1, g], v[k0:k1, g], scale=scale,
                               q_rope=q_rope[q0:q1, h] if q_rope is not None else None,
                               k_rope=k_rope[k0:k1, g] if k_rope is not None else None,
-                              mask=atten_mask[:q1 - q0, :k1 - k0] if atten_mask is not None else None,
+                              mask=_tnd_mask(atten_mask, q1 - q0, k1 - k0) if atten_mask is not None else None,
                               causal=causal, pre_tokens=pre_tokens, next_tokens=next_tokens,
                               sink=float(sink[h]) if sink is not None else None, rows=rows,
                               pse=pse_block(bi, h), q_start=q_start, kv_start=kv_start)

@@ -137,6 +137,42 @@ def pin_brute_force_varlen(orc):
                 _close(L[h, sl_q], torch.tensor(l, dtype=F64), tag + " l")
 
 
+def pin_tnd_mask_smaller_than_sequences(orc):
+    """A 2-D TND mask smaller than some sequences: positions beyond its rows or
+    columns are excluded (reading of the V5 parameter table, row
+    attenMaskOptional).  The brute force builds each sequence's mask cell by
+    cell: inside the mask it is the mask's byte, outside it is 1."""
+    g = torch.Generator().manual_seed(19)
+    lq, lk = [6, 2, 7, 3], [5, 4, 7, 1]
+    N, D, Dv = 2, 4, 3
+    Tq, Tk = sum(lq), sum(lk)
+    q, k, v = _rand((Tq, N, D), g), _rand((Tk, N, D), g), _rand((Tk, N, Dv), g)
+    sink = _rand((N,), g)
+    cq = [0] + list(itertools.accumulate(lq))
+    ck = [0] + list(itertools.accumulate(lk))
+    mr, mc = 4, 3  # smaller than sequences 0 and 2 in both directions
+    mask2d = (torch.rand(mr, mc, generator=g) < 0.3).to(torch.uint8)
+    mask2d[0, 0] = 0  # row 0 keeps key 0 inside the mask
+    ml = mask2d.tolist()
+    for causal, use_sink in itertools.product((False, True), (False, True)):
+        O, M, L = orc.attention_forward(q, k, v, layout="TND", scale=0.7, sink=sink if use_sink else None,
+                                        causal=causal, atten_mask=mask2d, cu_seqlens_q=cq, cu_seqlens_kv=ck)
+        for b in range(len(lq)):
+            ms = [[ml[i][j] if (i < mr and j < mc) else 1 for j in range(lk[b])] for i in range(lq[b])]
+            for h in range(N):
+                sl_q, sl_k = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+                o, m, l = brute.head(q[sl_q, h].tolist(), k[sl_k, h].tolist(), v[sl_k, h].tolist(), 0.7,
+                                     mask=ms, causal=causal, sink=float(sink[h]) if use_sink else None)
+                tag = f"tnd small mask b={b} h={h} causal={causal} sink={use_sink}"
+                _close(O[sl_q, h], torch.tensor(o, dtype=F64), tag + " O")
+                _close(M[h, sl_q], torch.tensor(m, dtype=F64), tag + " m")
+                _close(L[h, sl_q], torch.tensor(l, dtype=F64), tag + " l")
+        # rows past the mask's extent keep no key: O = 0 and, without a sink, m = -inf and l = 0
+        if not use_sink:
+            assert bool((M[:, cq[0] + mr:cq[1]] == float("-inf")).all()), "rows beyond the mask must be empty"
+            assert bool((O[cq[0] + mr:cq[1]] == 0).all())
+
+
 # ---------------------------------------------------------------------------
 # 2. Reductions to torch's scaled_dot_product_attention (float64, CPU)
 # ---------------------------------------------------------------------------

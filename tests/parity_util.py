@@ -44,6 +44,38 @@ def to_gpu(t: Optional[torch.Tensor], dev="cuda:0"):
     return None if t is None else t.to(dev)
 
 
+def run_gpu_poisoned(case: synth.Case, dev="cuda:0"):
+    """Run the library on the case with O and both statistics pre-filled with NaN,
+    so that an element the kernels never write stays NaN; returns CPU tensors
+    (O, softmax_max, softmax_sum)."""
+    g = {k: to_gpu(v, dev) for k, v in case.tensors().items()}
+    q = g["q"]
+    out = torch.full(q.shape[:-1] + (case.v.shape[-1],), float("nan"), dtype=q.dtype, device=dev)
+    if case.layout == "TND":
+        T, N = q.shape[0], q.shape[1]
+        shp = (T, N, 8) if case.softmax_out_layout == "same_as_input" else (N, T, 8)
+        N_ = N
+    else:
+        B = q.shape[0]
+        N_ = q.shape[1] if case.layout == "BNSD" else q.shape[2]
+        S = q.shape[2] if case.layout == "BNSD" else q.shape[1]
+        shp = (B, N_, S, 8)
+    smax = torch.full(shp, float("nan"), dtype=torch.float32, device=dev)
+    ssum = torch.full(shp, float("nan"), dtype=torch.float32, device=dev)
+    plan = api.ForwardPlan(q, g["k"], g["v"], layout=case.layout, scale=case.scale, head_num=N_,
+                           query_rope=g["q_rope"], key_rope=g["k_rope"], atten_mask=g["atten_mask"], sink=g["sink"],
+                           cu_seqlens_q=g["cu_seqlens_q"], cu_seqlens_kv=g["cu_seqlens_kv"], causal=case.causal,
+                           pre_tokens=case.pre_tokens, next_tokens=case.next_tokens,
+                           softmax_out_layout=case.softmax_out_layout, out=out, softmax_max=smax, softmax_sum=ssum,
+                           real_shift=g["pse"])
+    try:
+        plan.run()
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    return out.cpu(), smax.cpu(), ssum.cpu()
+
+
 def run_gpu(case: synth.Case, *, stats: bool = True, layout_heads: Optional[int] = None, dev="cuda:0"):
     """Run the library on the case; returns CPU tensors (O, softmax_max, softmax_sum)."""
     g = {k: to_gpu(v, dev) for k, v in case.tensors().items()}

@@ -459,6 +459,41 @@ def test_two_group_kernel_needs_32bit_row_offsets(monkeypatch):
     assert st == 561103 and pl is None and "2 GiB" in _lib.last_error_message()
 
 
+def test_four_wave_kernel_needs_32bit_block_offsets(monkeypatch):
+    # the four-wave kernel stages a 64-row key block with 32-bit byte offsets: 64 x the row stride in bytes
+    # must stay below 2^31; a strided K with 2^25-byte rows reaches it, one 8-element step less does not
+    q = desc([1, 256, 2, 128])
+    far = desc([1, 256, 2, 128], strides=[2**25, 2**24, 128, 1])          # 2^24 elements = 2^25 bytes per row
+    near = desc([1, 256, 2, 128], strides=[2**25, 2**24 - 8, 128, 1])
+    st, _, pl = plan(q, far, q, q)
+    assert st == 0, _lib.last_error_message()
+    assert "kernel=generic" in describe(pl), describe(pl)
+    _lib.fa_plan_destroy(pl)
+    st, _, pl = plan(q, near, q, q)
+    assert st == 0 and "kernel=mfma " in describe(pl), describe(pl)
+    _lib.fa_plan_destroy(pl)
+    st, _, pl = plan(q, q, far, q)  # the same bound holds for V
+    assert st == 0 and "kernel=generic" in describe(pl), describe(pl)
+    _lib.fa_plan_destroy(pl)
+    monkeypatch.setenv("FA_FWD_KERNEL", "mfma")
+    st, _, pl = plan(q, far, q, q)
+    assert st == 561103 and pl is None and "32-bit block offsets" in _lib.last_error_message()
+
+
+def test_pse_lds_needs_32bit_tile_offsets():
+    # the pse tile (128 rows) is read with 32-bit byte offsets: 128 x the row stride in bytes below 2^31
+    B, N, S, D = 1, 2, 256, 128
+    q = desc([B, N, S, D])
+    ok = desc([B, N, S, S], strides=[N * S * (2**23 - 8), S * (2**23 - 8), 2**23 - 8, 1])
+    far = desc([B, N, S, S], strides=[N * S * 2**23, S * 2**23, 2**23, 1])
+    st, _, pl = plan(q, q, q, q, pse=ok, layout=b"BNSD")
+    assert st == 0 and "pse_lds=1" in describe(pl), describe(pl)
+    _lib.fa_plan_destroy(pl)
+    st, _, pl = plan(q, q, q, q, pse=far, layout=b"BNSD")
+    assert st == 0 and "pse_lds=0" in describe(pl), describe(pl)
+    _lib.fa_plan_destroy(pl)
+
+
 @pytest.mark.parametrize("dr", [0, 64])
 def test_d96_on_matrix_cores(dr, monkeypatch):
     s = [2, 1024, 8, 96]

@@ -46,6 +46,10 @@ MUTANTS = {
                       "w = torch.where(torch.isfinite(ms), torch.exp(ms - m_safe), torch.zeros_like(ls))"),
     "merge_sign": ("w = torch.where(torch.isfinite(ms), torch.exp(ms - m_safe) * ls, torch.zeros_like(ls))",
                    "w = torch.where(torch.isfinite(ms), torch.exp(m_safe - ms) * ls, torch.zeros_like(ls))"),
+    "tnd_mask_outside_kept": ("    out = torch.ones(lq, lk, dtype=atten_mask.dtype)\n",
+                              "    out = torch.zeros(lq, lk, dtype=atten_mask.dtype)\n"),
+    "tnd_mask_outside_wraps": ("    out[:r, :c] = atten_mask[:r, :c]\n",
+                               "    out[:r, :c] = atten_mask[:r, :c]\n    out[r:, :c] = atten_mask[:lq - r, :c] if lq - r <= atten_mask.shape[0] else out[r:, :c]\n"),
     "stats_layout_transposed": ("    if layout == \"TND\" and softmax_out_layout == \"same_as_input\":\n        x = x.transpose(0, 1)\n",
                                 "    if layout == \"TND\" and softmax_out_layout == \"\":\n        x = x.transpose(0, 1)\n"),
 }

@@ -112,6 +112,17 @@ SMALL = {
     "mask_inside_band": lambda: _mask_inside_band_case(86),
     "mask_outside_band": lambda: _mask_outside_band_case(87),
     "tnd_mask_blocks": lambda: _tnd_block_mask_case(88),
+    # a 2-D TND mask smaller than the longer sequences: positions beyond it are excluded
+    "tnd_mask_shorter_than_sequence": lambda: _tnd_small_mask_case(89),
+    "tnd_mask_shorter_causal_sink": lambda: _tnd_small_mask_case(94, causal=True, sink=True),
+    # head dim 256 (and Dv 256 or below it)
+    "d256_causal_bf16": lambda: synth.dense_case("x", "BNSD", 1, 2, 200, 256, "bf16", 120, causal=True, skv=333),
+    "d256_varlen_sink_fp16": lambda: synth.varlen_case("x", [130, 0, 257, 64], 2, 256, "fp16", 121, sink=True,
+                                                       causal=True),
+    "d256_gqa_bsnd": lambda: synth.dense_case("x", "BSND", 1, 4, 150, 256, "bf16", 122, nkv=2, skv=270),
+    "d256_gqa_fp32": lambda: synth.dense_case("x", "BSND", 1, 4, 90, 256, "fp32", 123, nkv=1, causal=True),
+    "d256_dv128_band_mask": lambda: _band_mask_case(124, 70, 9, d=256, dv=128),
+    "d256_dv256_mask_blocks_sink": lambda: _block_mask_case(125, 128, 64, (1, 1), d=256, sink=True, skv=400),
 }
 
 
@@ -120,6 +131,10 @@ def _block_mask_case(seed, rb, cb, bn, *, dtype="bf16", d=128, drope=0, sink=Fal
     plus one fully excluded row; 700 rows and skv keys."""
     c = synth.dense_case("x", "BNSD", 2, 2, 700, d, dtype, seed, skv=skv, drope=drope, sink=sink,
                          pse="full" if pse else None)
+    return _add_block_mask(c, seed, rb, cb, bn, skv)
+
+
+def _add_block_mask(c, seed, rb, cb, bn, skv):
     g = synth.generator(seed + 1000)
     nr, nc = -(-700 // rb), -(-skv // cb)
     kind = torch.rand(bn[0], bn[1], nr, nc, generator=g)
@@ -194,8 +209,8 @@ def _pse_band_mask_case(seed):
     return c
 
 
-def _band_mask_case(seed, pre, nxt, dtype="bf16", d=128):
-    c = synth.dense_case("x", "BNSD", 1, 2, 230, d, dtype, seed)
+def _band_mask_case(seed, pre, nxt, dtype="bf16", d=128, dv=None):
+    c = synth.dense_case("x", "BNSD", 1, 2, 230, d, dtype, seed, dv=dv)
     i = torch.arange(230).view(-1, 1)
     j = torch.arange(230).view(1, -1)
     c.atten_mask = (((j - i) > nxt) | ((i - j) > pre)).to(torch.uint8)  # consistent with the window
@@ -208,6 +223,19 @@ def _random_mask_case(seed, bn):
     g = synth.generator(seed + 1000)
     c.atten_mask = (torch.rand(bn[0], bn[1], 150, 150, generator=g) < 0.5).to(torch.bool)
     c.atten_mask[..., 7, :] = True  # a row with no kept key
+    return c
+
+
+def _tnd_small_mask_case(seed, causal=False, sink=False):
+    """Sequences of 300, 0, 17 and 260 rows against a [200, 150] TND mask: the
+    rows and keys of the long sequences beyond it are excluded."""
+    c = synth.varlen_case("x", [300, 0, 17, 260], 2, 128, "bf16", seed, causal=causal, sink=sink)
+    g = synth.generator(seed + 1000)
+    i = torch.arange(200).view(-1, 1)
+    j = torch.arange(150).view(1, -1)
+    m = (torch.rand(200, 150, generator=g) < 0.2) | (((i // 128) + (j // 64)) % 3 == 1)
+    m[:, 0] = False  # every row inside the mask keeps key 0
+    c.atten_mask = m.to(torch.uint8)
     return c
 
 
@@ -501,22 +529,36 @@ def test_full_size_sampled(name):
     case = _full_case(name)
     print(f"[parity] full {name} q={tuple(case.q.shape)}", flush=True)
     with pu.forced_kernel("auto"):
-        o, smax, ssum = pu.run_gpu(case)
+        # outputs start as NaN: an element no kernel writes fails the checks below
+        o, smax, ssum = pu.run_gpu_poisoned(case)
     g = synth.generator(999)
     if case.layout == "TND":
         cu = case.cu_seqlens_q.tolist()
         nseq, nh = len(cu) - 1, case.q.shape[1]
         samples = []
-        for b in sorted({0, nseq - 1, nseq // 2}):
-            for h in sorted({0, nh - 1}):
-                samples.append((b, h, pu.sample_rows(cu[b + 1] - cu[b], 12, g)))
+        for b in range(nseq):
+            n = cu[b + 1] - cu[b]
+            for h in range(nh):
+                if b in (0, nseq // 2, nseq - 1) and h in (0, nh - 1):
+                    samples.append((b, h, pu.sample_rows(n, 12, g)))
+                elif n > 0:  # the first and last row of every (sequence, head)
+                    samples.append((b, h, torch.tensor(sorted({0, n - 1}), dtype=torch.int64)))
     else:
         B = case.q.shape[0]
         nh = case.q.shape[1] if case.layout == "BNSD" else case.q.shape[2]
         S = case.q.shape[2] if case.layout == "BNSD" else case.q.shape[1]
-        samples = [(b, h, pu.sample_rows(S, 12, g)) for b in sorted({0, B - 1}) for h in sorted({0, nh // 2, nh - 1})]
+        samples = []
+        for b in range(B):
+            for h in range(nh):
+                if b in (0, B - 1) and h in (0, nh // 2, nh - 1):
+                    samples.append((b, h, pu.sample_rows(S, 12, g)))
+                else:  # edge rows of every (batch, head): first, tile boundaries, last
+                    samples.append((b, h, torch.tensor(sorted({0, 255, 256, S - 1}), dtype=torch.int64)))
     _report(name, pu.compare_sampled(case, samples, o, smax, ssum))
-    # properties at every row: finite, stats slots equal, l >= 1 where a key is kept
+    # every element written (the NaN fill is gone), then properties at every row:
+    # finite output, stats slots equal, l >= 1 where a key is kept
+    assert not bool(torch.isnan(o.float()).any()), "output elements left unwritten"
+    assert not bool(torch.isnan(smax).any()) and not bool(torch.isnan(ssum).any()), "statistics left unwritten"
     assert torch.isfinite(o.float()).all()
     assert bool((smax == smax[..., :1]).all()) and bool((ssum == ssum[..., :1]).all())
     assert bool((ssum[..., 0] >= 1.0 - 1e-6).all())
