@@ -14,7 +14,9 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_fwd.so")
+# FA_FWD_LIB names another build of the same C ABI (the tests use it for a host-only
+# AddressSanitizer build of phase 1); by default the in-tree library.
+LIB_PATH = os.environ.get("FA_FWD_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_fwd.so")
 
 FA_OK = 0
 FA_ERR_PARAM_NULLPTR = 161001
@@ -34,7 +36,7 @@ FA_DTYPE = {
 }
 
 EXPORTED = ("fa_fwd_get_workspace_size", "fa_fwd", "fa_fwd_merge", "fa_plan_destroy", "fa_plan_describe",
-            "fa_last_error_message")
+            "fa_last_error_message", "fa_clock_probe")
 
 
 class FaTensor(ctypes.Structure):
@@ -89,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_merge.restype = ctypes.c_int32
         L.fa_fwd_merge.argtypes = [ctypes.c_int32, T, T, T, ctypes.c_char_p, ctypes.c_int64, ctypes.c_char_p,
                                    T, T, T, ctypes.c_void_p]
+        L.fa_clock_probe.restype = ctypes.c_int32
+        L.fa_clock_probe.argtypes = [ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
         L.fa_last_error_message.restype = ctypes.c_char_p
         L.fa_last_error_message.argtypes = []
         _lib = L
@@ -188,3 +192,12 @@ def fa_plan_describe(plan) -> str:
     buf = ctypes.create_string_buffer(n + 1)
     L.fa_plan_describe(plan, buf, n + 1)
     return buf.value.decode()
+
+
+def fa_clock_probe(microseconds: int, device_out: torch.Tensor, stream: int) -> None:
+    """Enqueue the shader-clock probe; ``device_out`` is a GPU int64 tensor of 2 elements."""
+    if device_out.dtype != torch.int64 or device_out.numel() < 2 or not device_out.is_cuda:
+        raise ValueError("device_out must be a GPU int64 tensor with 2 elements")
+    st = lib().fa_clock_probe(int(microseconds), device_out.data_ptr(), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_clock_probe", last_error_message())

@@ -153,6 +153,25 @@ __global__ void __launch_bounds__(256) mask_classify(const uint8_t* __restrict__
   if (threadIdx.x == 0) cls[id] = any_alive ? (any_relevant ? CLS_MIXED : CLS_KEPT) : CLS_EXCLUDED;
 }
 
+// Shader-clock probe: one wave reads the shader clock counter (s_memtime)
+// and the constant 100 MHz counter (s_memrealtime) while it idles for `ticks`
+// of the latter (or at most `cap` sleep rounds), then writes both deltas.
+__global__ void __launch_bounds__(64) clock_probe(unsigned long long ticks, unsigned int cap,
+                                                 unsigned long long* __restrict__ out) {
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+  unsigned long long r = r0;
+  for (unsigned int n = 0; r - r0 < ticks && n < cap; ++n) {
+    __builtin_amdgcn_s_sleep(8);
+    r = __builtin_amdgcn_s_memrealtime();
+  }
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+  if (threadIdx.x == 0) {
+    out[0] = c1 - c0;
+    out[1] = r - r0;
+  }
+}
+
 }  // namespace fa
 
 namespace {
@@ -239,5 +258,25 @@ extern "C" fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_p
     e = fa::launch_split_merge(p, plan->dtype, s);
     if (e != hipSuccess) return runtime_fail("key split merge launch", e);
   }
+  return FA_OK;
+}
+
+extern "C" fa_status fa_clock_probe(uint32_t microseconds, unsigned long long* device_out, void* stream) {
+  if (!device_out) {
+    fa_set_error("device_out is NULL");
+    return FA_ERR_PARAM_NULLPTR;
+  }
+  if (microseconds < 1 || microseconds > 1000000) {
+    fa_set_error("microseconds must be in 1..1000000");
+    return FA_ERR_UNSUPPORTED;
+  }
+  unsigned long long ticks = 100ull * microseconds;  // 100 MHz counter
+  // one sleep round is at least 8 x 64 shader cycles (over 0.1 us at up to
+  // 3 GHz), so this many rounds outlast the interval with room to spare
+  unsigned int cap = 20u * microseconds + 1000u;
+  void* args[] = {(void*)&ticks, (void*)&cap, (void*)&device_out};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::clock_probe), dim3(1), dim3(64), args, 0,
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return runtime_fail("clock probe launch", e);
   return FA_OK;
 }

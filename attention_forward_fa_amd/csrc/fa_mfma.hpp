@@ -51,12 +51,12 @@ __device__ __forceinline__ f32x16 mfma32<_Float16>(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-template <typename T, int D, int DR>
+template <typename T, int D, int DR, int DVAL>
 struct MfmaCfg {
   static constexpr int BM = kMfmaBM;       // query rows per workgroup
   static constexpr int BN = kMfmaBN;       // keys per step
   static constexpr int DK = D + DR;        // score reduction length
-  static constexpr int DV = D;
+  static constexpr int DV = DVAL;          // value / output columns
   static constexpr int KU = D / 8;         // 16-byte units per K row
   static constexpr int KRU = DR / 8;       // units per Krope row
   static constexpr int VU = DV / 8;        // units per V row
@@ -71,6 +71,11 @@ struct MfmaCfg {
   static constexpr int V_LOADS = BN * VU / kMfmaThreads;
   static constexpr int NKS = DK / 16;                        // MFMA k-steps of the score product
   static constexpr int NDT = DV / 32;                        // 32-wide output tiles
+  // Workgroups per CU: two while both stages fit in 80 KiB of LDS (the pse
+  // tile, 16 KiB, comes only without rope, where a stage is at most 32 KiB);
+  // wider heads (D = 256) run one, which also lets a wave hold up to 512
+  // registers (the output accumulator then lives in the AGPRs).
+  static constexpr int OCC = 2 * STAGE_BYTES <= 80 * 1024 ? 2 : 1;
 };
 
 // Physical 16-byte unit of logical unit u in LDS row r (the LDS serves 256
@@ -186,9 +191,9 @@ __device__ __forceinline__ void dma16(const void* base, int64_t nbytes, lds_void
 // Load n of wave w fills LDS units [64 (4n + w), +64): lane l writes unit
 // 64 (4n + w) + l, i.e. row unit / U at physical unit unit % U, which holds the
 // logical unit the swizzle maps there.
-template <typename T, int D, int DR>
+template <typename T, int D, int DR, int DV>
 __device__ __forceinline__ void stage_block(char* __restrict__ st, int jb, const LoopCtx<T>& x) {
-  using C = MfmaCfg<T, D, DR>;
+  using C = MfmaCfg<T, D, DR, DV>;
   const int64_t rows = min(x.skv - jb, C::BN);  // >= 1 for every visited block
   const T* kb = x.kbase + (int64_t)jb * (x.krow_b / (int64_t)sizeof(T));
 #pragma unroll
@@ -331,14 +336,14 @@ __device__ __forceinline__ void pse_read(uint2 (&pw)[8], const char* tile, const
 // Excluded positions are applied before the score product: the accumulators
 // start at 0 for kept and -inf for excluded elements, and the MFMA adds K Q^T
 // to them (-inf + finite = -inf).  Nothing branches after the scores.
-template <typename T, int D, int DR, bool PL>
+template <typename T, int D, int DR, int DV, bool PL>
 __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __restrict__ nxt,
                                           char* __restrict__ ptile, int jb, bool more, const Params& p,
                                           const LoopCtx<T>& x,
-                                          const typename Vec8<T>::type (&qf)[MfmaCfg<T, D, DR>::NKS],
-                                          f32x16 (&oacc)[MfmaCfg<T, D, DR>::NDT], float& m_ref, float& m_max,
+                                          const typename Vec8<T>::type (&qf)[MfmaCfg<T, D, DR, DV>::NKS],
+                                          f32x16 (&oacc)[MfmaCfg<T, D, DR, DV>::NDT], float& m_ref, float& m_max,
                                           float& lsum, uint32_t (&mw)[8], uint2 (&pw)[8]) {
-  using C = MfmaCfg<T, D, DR>;
+  using C = MfmaCfg<T, D, DR, DV>;
   using V8 = typename Vec8<T>::type;
   constexpr int BN = C::BN;
   const int l32 = x.l32, hh = x.hh, row = x.row;
@@ -410,7 +415,7 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
   }
 
   if (more) {
-    stage_block<T, D, DR>(nxt, jb + BN, x);
+    stage_block<T, D, DR, DV>(nxt, jb + BN, x);
     if (block_kind(p, jb + BN, x).read_mask) fetch_mask(mw, p, jb + BN, x);
     if constexpr (!PL && DR == 0) {
       if (p.has_pse) fetch_pse(pw, p, jb + BN, x);
@@ -496,10 +501,12 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
   __builtin_amdgcn_s_setprio(0);
 }
 
-// PL: pse staged through LDS (dense pse with 16-byte aligned rows, no rope).
-template <typename T, int D, int DR, bool PL = false>
-__global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
-  using C = MfmaCfg<T, D, DR>;
+// D: score dims from q / k, DR: score dims from the rope tensors, DV: value
+// and output dims.  PL: pse staged through LDS (dense pse with 16-byte
+// aligned rows, no rope).
+template <typename T, int D, int DR, int DV, bool PL = false>
+__global__ void __launch_bounds__(kMfmaThreads, (MfmaCfg<T, D, DR, DV>::OCC)) fa_fwd_mfma(const Params p) {
+  using C = MfmaCfg<T, D, DR, DV>;
   using V8 = typename Vec8<T>::type;
   constexpr int BM = C::BM, BN = C::BN;
   static_assert(!PL || DR == 0, "pse and rope do not combine");
@@ -596,7 +603,7 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
 #pragma unroll
   for (int w = 0; w < 8; ++w) pw[w] = make_uint2(0, 0);
   if (nblocks > 0) {
-    stage_block<T, D, DR>(smem, jb0, x);
+    stage_block<T, D, DR, DV>(smem, jb0, x);
     if (block_kind(p, jb0, x).read_mask) fetch_mask(mw, p, jb0, x);
     if constexpr (PL) {
       pse_stage<T>(ptile, p, jb0, x);
@@ -614,7 +621,7 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   for (int it = 0; it < nblocks; ++it) {
     const int stg = it & 1;
     const bool more = it + 1 < nblocks;
-    key_block<T, D, DR, PL>(smem + stg * C::STAGE_BYTES, smem + (stg ^ 1) * C::STAGE_BYTES, ptile, jb0 + it * BN,
+    key_block<T, D, DR, DV, PL>(smem + stg * C::STAGE_BYTES, smem + (stg ^ 1) * C::STAGE_BYTES, ptile, jb0 + it * BN,
                             more, p, x, qf, oacc, m_ref, m_max, lsum, mw, pw);
     // this thread's loads of the next block landed; then everyone's, before the swap
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
@@ -633,7 +640,7 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
     // range's statistics (max, sum at that max), merged by a later pass
     if (!row_ok) return;
     const int64_t prow = ((int64_t)(tl.split * p.nbatch + tl.b) * p.nq + tl.h) * p.sq + row;
-    float* po = p.part_o + prow * D;
+    float* po = p.part_o + prow * DV;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -650,7 +657,7 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) fa_fwd_mfma(const Params p) {
   }
   {
     T* obase = static_cast<T*>(p.o) + tl.b * p.o_sb + tl.h * p.o_sh + (tl.q_row0 + i0) * p.o_ss;
-    o_tile_store<T, D, kMfmaThreads>(smem, oacc, inv, wave * 32 + l32, hh, obase, p.o_ss, max(min(BM, tl.sq - i0), 0));
+    o_tile_store<T, DV, kMfmaThreads>(smem, oacc, inv, wave * 32 + l32, hh, obase, p.o_ss, max(min(BM, tl.sq - i0), 0));
   }
   if (!row_ok) return;
   const int64_t orow = tl.q_row0 + row;

@@ -355,8 +355,12 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   int64_t max_row_b = (k.ss > v.ss ? k.ss : v.ss) * esz_in;
   if (query_rope && kr.ss * esz_in > max_row_b) max_row_b = kr.ss * esz_in;
   const bool block_offsets_fit = (int64_t)fa::kMfmaBN * max_row_b < ((int64_t)1 << 31);
-  const bool mfma_shape = (dt == FA_DTYPE_F16 || dt == FA_DTYPE_BF16) && (dmain == 64 || dmain == 96 || dmain == 128) &&
-                          v.d == dmain && (drm == 0 || drm == 64) && vec_ok(query->data, q) && vec_ok(key->data, k) &&
+  // (D, Dr, Dv) the four-wave kernel is built for: Dv == D in {64, 96, 128}
+  // with 0 or 64 rope dims; D = 256 (no rope) with Dv = 256 or 128
+  const bool dims_mfma = ((dmain == 64 || dmain == 96 || dmain == 128) && v.d == dmain && (drm == 0 || drm == 64)) ||
+                         (dmain == 256 && drm == 0 && (v.d == 256 || v.d == 128));
+  const bool mfma_shape = (dt == FA_DTYPE_F16 || dt == FA_DTYPE_BF16) && dims_mfma && vec_ok(query->data, q) &&
+                          vec_ok(key->data, k) &&
                           vec_ok(value->data, v) && vec_ok(attention_out->data, o) &&
                           (!query_rope || (vec_ok(query_rope->data, qr) && vec_ok(key_rope->data, kr))) && stats_vec;
   const bool mfma_ok = mfma_shape && block_offsets_fit;
@@ -399,9 +403,9 @@ extern "C" fa_status fa_fwd_get_workspace_size(
         delete pl;
         return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL=pp: the two-group kernel takes no real_shift");
       }
-      if (!strcmp(force, "pp") && dmain == 96) {
+      if (!strcmp(force, "pp") && !((dmain == 64 || dmain == 128) && v.d == dmain)) {
         delete pl;
-        return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL=pp: the two-group kernel has D = 64 and 128 only");
+        return fail(FA_ERR_UNSUPPORTED, "FA_FWD_KERNEL=pp: the two-group kernel has D = Dv = 64 or 128 only");
       }
       if (!strcmp(force, "pp") && !pp_fits) {
         delete pl;
@@ -548,7 +552,9 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   p.part_o = p.part_ml = nullptr;
   pl->ws_part_off = 0;
   if (kind == fa::KERNEL_MFMA && !p.varlen && wg > 0 && k.s > 0) {
-    int64_t want = fa::kWgSlots / wg;
+    // workgroup slots of the chip: two per CU, one for D = 256 (its LDS stages take 128 KiB)
+    const int64_t slots = dmain == 256 ? fa::kNumCUs : fa::kWgSlots;
+    int64_t want = slots / wg;
     if (want > fa::kMaxKvSplits) want = fa::kMaxKvSplits;
     const int64_t max_by_len = k.s / ((int64_t)fa::kMinSplitBlocks * pl->bn);
     if (want > max_by_len) want = max_by_len;
@@ -611,6 +617,15 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   p.num_wg = (int32_t)wg;
   *workspace_size = pl->ws_bytes;
   *plan = pl;
+  // FA_LOG (set and not "0"): one line per plan on stderr with the kernel,
+  // tile, grid and workspace phase 1 chose
+  if (const char* log = getenv("FA_LOG")) {
+    if (log[0] != '\0' && strcmp(log, "0") != 0) {
+      char buf[512];
+      fa_plan_describe(pl, buf, sizeof(buf));
+      fprintf(stderr, "[fa_fwd] plan %s layout=%s\n", buf, input_layout);
+    }
+  }
   return FA_OK;
 }
 

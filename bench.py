@@ -14,6 +14,13 @@ kept pairs counted on 128x128 blocks as the workloads' accounting asks.
 events on the launch stream during the timed region, against the MI355X dense
 matrix peak.  ``cpu_baseline`` times the CPU float64 oracle on a bounded
 sample of the same workload.
+
+After the timed region (never inside it) the line also gets: the per-launch
+p10 / p90, a cold-cache figure (each call after 512 MiB are written, so the
+inputs are out of the 256 MiB last-level cache), the shader clock measured
+while the forward runs back to back (``sclk_mhz_under_load``, from the
+library's clock probe), and for the 16-bit dense workloads the same workload
+in the other 16-bit type (``companion``).
 """
 from __future__ import annotations
 
@@ -33,8 +40,12 @@ METRIC = "attention fwd TFLOP/s + % of MI355X bf16 MFMA peak, B2 S4096 N24 D128"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 HBM_GBPS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-KERNEL_SOURCES = ["fa_mfma.hpp", "fa_mfma_pp.hpp", "fa_device.hpp", "fa_params.h", "fa_mfma_bf16.hip",
+KERNEL_SOURCES = ["fa_mfma.hpp", "fa_mfma_pp.hpp", "fa_mfma_dispatch.hpp", "fa_device.hpp", "fa_params.h", "fa_mfma_bf16.hip",
                   "fa_mfma_f16.hip", "fa_generic.hip", "fa_launch.hip", "fa_merge.hip"]
+
+
+# workloads whose element type --dtype chooses (the rest fix theirs)
+DTYPE_WORKLOADS = ("c2_dense_bsnd", "c2_gqa_nkv4", "c2_mqa", "d256_dense_bsnd")
 
 
 def kernel_source_hash() -> str:
@@ -52,11 +63,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2_dense_bsnd",
                     choices=["c2_dense_bsnd", "c3_causal", "c3_band", "c4_varlen_causal", "c5_varlen_sink_rope",
-                             "c6_dense_pse", "c7_outer_split"])
+                             "c6_dense_pse", "c7_outer_split", "c2_gqa_nkv4", "c2_mqa", "d256_dense_bsnd"])
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold", action="store_true", help="also time the kernel after evicting caches")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache figure")
+    ap.add_argument("--no-clock", action="store_true", help="skip the shader-clock reading under load")
+    ap.add_argument("--no-companion", action="store_true", help="skip the other 16-bit type's figure")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="launch one device copy of this many MiB (counter calibration runs)")
     return ap.parse_args()
@@ -199,6 +212,136 @@ def cpu_baseline(case, budget_s: float):
 # main
 # ---------------------------------------------------------------------------
 
+class Runner:
+    """One workload resident on the GPU: its tensors, outputs, workspace and one step (phase 1 + phase 2)."""
+
+    def __init__(self, case, workload, dev):
+        import torch
+
+        from attention_forward_fa_amd import _lib, api
+
+        import synth
+
+        self.case, self.torch, self._lib = case, torch, _lib
+        g = {k: (v.to(dev) if v is not None else None) for k, v in case.tensors().items()}
+        self.g = g
+        self.nheads = case.q.shape[1] if case.layout in ("BNSD", "TND") else case.q.shape[2]
+        self.out = torch.empty(case.q.shape[:-1] + (case.v.shape[-1],), dtype=case.q.dtype, device=dev)
+        if case.layout == "TND":
+            self.smax = torch.empty(self.nheads, case.q.shape[0], 8, dtype=torch.float32, device=dev)
+        else:
+            B = case.q.shape[0]
+            S = case.q.shape[2] if case.layout == "BNSD" else case.q.shape[1]
+            self.smax = torch.empty(B, self.nheads, S, 8, dtype=torch.float32, device=dev)
+        self.ssum = torch.empty_like(self.smax)
+        self.stream = torch.cuda.current_stream(dev)
+        self.sh = self.stream.cuda_stream
+        plan0 = api.ForwardPlan(g["q"], g["k"], g["v"], layout=case.layout, scale=case.scale, head_num=self.nheads,
+                                query_rope=g["q_rope"], key_rope=g["k_rope"], atten_mask=g["atten_mask"],
+                                sink=g["sink"], cu_seqlens_q=g["cu_seqlens_q"], cu_seqlens_kv=g["cu_seqlens_kv"],
+                                causal=case.causal, pre_tokens=case.pre_tokens, next_tokens=case.next_tokens,
+                                softmax_out_layout=case.softmax_out_layout, out=self.out, softmax_max=self.smax,
+                                softmax_sum=self.ssum, real_shift=g["pse"])
+        self.desc = plan0.describe()
+        self.ws = plan0.workspace
+        plan0.close()
+        self.split = workload == "c7_outer_split"
+        self.merge_ev = []
+        if self.split:
+            # the c2 problem as an outer split along the keys: one call per key chunk, then the merge
+            cuts = synth.C7_CUTS
+            self.chunks = []
+            for a, b in zip(cuts[:-1], cuts[1:]):
+                self.chunks.append((a, g["k"][:, a:b], g["v"][:, a:b], torch.empty_like(self.out),
+                                    torch.empty_like(self.smax), torch.empty_like(self.ssum)))
+
+    def step(self, ev_pair=None):
+        case, g, _lib, sh, torch = self.case, self.g, self._lib, self.sh, self.torch
+        if self.split:
+            if ev_pair is not None:
+                ev_pair[0].record(self.stream)
+            for a, kc, vc, oc, mc, lc in self.chunks:
+                wsz, h = _lib.fa_fwd_get_workspace_size(
+                    g["q"], None, kc, None, vc, None, None, None, None, None, None, a, case.scale, 1.0,
+                    case.pre_tokens, case.next_tokens, self.nheads, case.layout, 0, 0, case.causal, "", mc, lc, oc)
+                _lib.fa_fwd(None, wsz, h, sh)
+                _lib.fa_plan_destroy(h)
+            if ev_pair is not None:
+                ev_pair[1].record(self.stream)
+                em = torch.cuda.Event(enable_timing=True)
+                em.record(self.stream)
+            _lib.fa_fwd_merge([c[3] for c in self.chunks], [c[4] for c in self.chunks], [c[5] for c in self.chunks],
+                              case.layout, self.nheads, "", self.out, self.smax, self.ssum, sh)
+            if ev_pair is not None:
+                em2 = torch.cuda.Event(enable_timing=True)
+                em2.record(self.stream)
+                self.merge_ev.append((em, em2))
+            return
+        # phase 1 + phase 2; the workspace is allocated once, outside the timed region
+        wsz, h = _lib.fa_fwd_get_workspace_size(
+            g["q"], g["q_rope"], g["k"], g["k_rope"], g["v"], g["pse"], g["atten_mask"], g["sink"], g["cu_seqlens_q"],
+            g["cu_seqlens_kv"], None, None, case.scale, 1.0, case.pre_tokens, case.next_tokens, self.nheads,
+            case.layout, 0, 0, case.causal, case.softmax_out_layout, self.smax, self.ssum, self.out)
+        if ev_pair is not None:
+            ev_pair[0].record(self.stream)
+        _lib.fa_fwd(self.ws, wsz, h, sh)
+        if ev_pair is not None:
+            ev_pair[1].record(self.stream)
+        _lib.fa_plan_destroy(h)
+
+    def timed(self, steps, warmup):
+        """W untimed steps, then K steps between two synchronisations: (wall seconds, per-launch ms list)."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(events[i])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        return elapsed, [a.elapsed_time(b) for a, b in events]
+
+    def cold(self, n, dev):
+        """Per-launch ms with the caches flushed first: 512 MiB written before each call (the last-level
+        cache holds 256 MiB), one call at a time."""
+        torch = self.torch
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        out = []
+        for _ in range(n):
+            flush.fill_(1)
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            self.step(ev)
+            torch.cuda.synchronize()
+            out.append(ev[0].elapsed_time(ev[1]))
+        del flush
+        return out
+
+    def clock_under_load(self, dev, window_us=150000):
+        """Shader clock while the forward runs back to back: the library's clock probe idles on a side
+        stream (default priority) for window_us while this stream keeps launching steps."""
+        torch, _lib = self.torch, self._lib
+        probe = torch.zeros(2, dtype=torch.int64, device=dev)
+        side = torch.cuda.Stream(device=dev)
+        for _ in range(3):
+            self.step()
+        torch.cuda.synchronize()
+        _lib.fa_clock_probe(window_us, probe, side.cuda_stream)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < window_us * 1.2e-6:
+            self.step()
+        torch.cuda.synchronize()
+        cycles, ticks = (int(x) for x in probe.cpu().tolist())
+        return cycles / (ticks / 100e6) / 1e6 if ticks > 0 else None
+
+
+def pct(xs, q):
+    ys = sorted(xs)
+    return ys[min(len(ys) - 1, max(0, int(round(q / 100.0 * (len(ys) - 1)))))]
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -210,34 +353,14 @@ def main():
     import torch
 
     import synth
-    from attention_forward_fa_amd import _lib, api
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    case = synth.workload(args.workload, args.dtype) if args.workload == "c2_dense_bsnd" else \
-        synth.workload(args.workload)
+    dtype_choice = args.workload in DTYPE_WORKLOADS
+    case = synth.workload(args.workload, args.dtype) if dtype_choice else synth.workload(args.workload)
     dtype = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[case.q.dtype]
-    g = {k: (v.to(dev) if v is not None else None) for k, v in case.tensors().items()}
-    nheads = case.q.shape[1] if case.layout in ("BNSD", "TND") else case.q.shape[2]
-    out = torch.empty(case.q.shape[:-1] + (case.v.shape[-1],), dtype=case.q.dtype, device=dev)
-    if case.layout == "TND":
-        T = case.q.shape[0]
-        smax = torch.empty(nheads, T, 8, dtype=torch.float32, device=dev)
-    else:
-        B = case.q.shape[0]
-        S = case.q.shape[2] if case.layout == "BNSD" else case.q.shape[1]
-        smax = torch.empty(B, nheads, S, 8, dtype=torch.float32, device=dev)
-    ssum = torch.empty_like(smax)
-
-    def make_plan():
-        return api.ForwardPlan(g["q"], g["k"], g["v"], layout=case.layout, scale=case.scale, head_num=nheads,
-                               query_rope=g["q_rope"], key_rope=g["k_rope"], atten_mask=g["atten_mask"],
-                               sink=g["sink"], cu_seqlens_q=g["cu_seqlens_q"], cu_seqlens_kv=g["cu_seqlens_kv"],
-                               causal=case.causal, pre_tokens=case.pre_tokens, next_tokens=case.next_tokens,
-                               softmax_out_layout=case.softmax_out_layout, out=out, softmax_max=smax,
-                               softmax_sum=ssum, real_shift=g["pse"])
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -248,69 +371,11 @@ def main():
         print(f"[bench] copy calibration: {args.copy_calibration_mib} MiB read + written", file=sys.stderr)
         del a, b
 
-    stream = torch.cuda.current_stream(dev)
-    sh = stream.cuda_stream
-    plan0 = make_plan()
-    desc = plan0.describe()
-    ws = plan0.workspace
-    plan0.close()
-
-    split = args.workload == "c7_outer_split"
-    if split:
-        # the c2 problem as an outer split along the keys: one call per key chunk, then the merge
-        cuts = synth.C7_CUTS
-        chunks = []
-        for a, b in zip(cuts[:-1], cuts[1:]):
-            chunks.append((a, g["k"][:, a:b], g["v"][:, a:b], torch.empty_like(out), torch.empty_like(smax),
-                           torch.empty_like(ssum)))
-        merge_ev = []
-
-    def step(ev_pair=None):
-        if split:
-            if ev_pair is not None:
-                ev_pair[0].record(stream)
-            for a, kc, vc, oc, mc, lc in chunks:
-                wsz, h = _lib.fa_fwd_get_workspace_size(
-                    g["q"], None, kc, None, vc, None, None, None, None, None, None, a, case.scale, 1.0,
-                    case.pre_tokens, case.next_tokens, nheads, case.layout, 0, 0, case.causal, "", mc, lc, oc)
-                _lib.fa_fwd(None, wsz, h, sh)
-                _lib.fa_plan_destroy(h)
-            if ev_pair is not None:
-                ev_pair[1].record(stream)
-                em = torch.cuda.Event(enable_timing=True)
-                em.record(stream)
-            _lib.fa_fwd_merge([c[3] for c in chunks], [c[4] for c in chunks], [c[5] for c in chunks], case.layout,
-                              nheads, "", out, smax, ssum, sh)
-            if ev_pair is not None:
-                em2 = torch.cuda.Event(enable_timing=True)
-                em2.record(stream)
-                merge_ev.append((em, em2))
-            return
-        # phase 1 + phase 2; the workspace is allocated once, outside the timed region
-        wsz, h = _lib.fa_fwd_get_workspace_size(
-            g["q"], g["q_rope"], g["k"], g["k_rope"], g["v"], g["pse"], g["atten_mask"], g["sink"], g["cu_seqlens_q"],
-            g["cu_seqlens_kv"], None, None, case.scale, 1.0, case.pre_tokens, case.next_tokens, nheads, case.layout, 0, 0,
-            case.causal, case.softmax_out_layout, smax, ssum, out)
-        if ev_pair is not None:
-            ev_pair[0].record(stream)
-        _lib.fa_fwd(ws, wsz, h, sh)
-        if ev_pair is not None:
-            ev_pair[1].record(stream)
-        _lib.fa_plan_destroy(h)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    kernel_ms = [a.elapsed_time(b) for a, b in events]
+    run = Runner(case, args.workload, dev)
+    desc = run.desc
+    elapsed, kernel_ms = run.timed(args.steps, args.warmup)
     kernel_ms_avg = sum(kernel_ms) / len(kernel_ms)
-    kernel_ms_med = sorted(kernel_ms)[len(kernel_ms) // 2]
+    kernel_ms_med = pct(kernel_ms, 50)
 
     pairs_blk = kept_pairs(case, block=128)
     pairs_exact = kept_pairs(case, block=0)
@@ -322,11 +387,11 @@ def main():
     src_hash = kernel_source_hash()
     traffic = load_traffic(src_hash, args.workload, dtype)
     abytes = algorithmic_bytes(case)
+    tf = lambda ms: round(flops / (ms * 1e-3) / 1e12, 2)
     # The dominant kernel's roofline: matrix-core bound when the workload's arithmetic intensity
     # (FLOP per algorithmic byte) is above the ridge point peak / HBM bandwidth, else HBM bound.
     if flops / abytes >= peak * 1e12 / (HBM_GBPS * 1e9):
-        roof = {"bound": "mfma", "achieved": round(flops / (kernel_ms_avg * 1e-3) / 1e12, 2), "peak": peak,
-                "unit": "TFLOP/s"}
+        roof = {"bound": "mfma", "achieved": tf(kernel_ms_avg), "peak": peak, "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": round(abytes / (kernel_ms_avg * 1e-3) / 1e9, 1), "peak": HBM_GBPS,
                 "unit": "GB/s"}
@@ -346,6 +411,7 @@ def main():
         "dtype": dtype,
         "data": "synthetic: iid N(0,1) q/k/v drawn in fp32 from a fixed seed, rounded to the dtype",
         "config": {"workload": args.workload, "layout": case.layout, "q_shape": list(case.q.shape),
+                   "kv_heads": case.k.shape[1] if case.layout in ("BNSD", "TND") else case.k.shape[2],
                    "causal": case.causal, "mask": case.atten_mask is not None,
                    "pre_tokens": case.pre_tokens, "next_tokens": case.next_tokens,
                    "rope_dim": case.q_rope.shape[-1] if case.q_rope is not None else 0,
@@ -354,34 +420,46 @@ def main():
         "roofline": roof,
         "kernel": {"name": "fa_fwd_" + desc.split()[0].split("=")[1], "plan": desc,
                    "avg_ms": round(kernel_ms_avg, 5), "median_ms": round(kernel_ms_med, 5),
+                   "p10_ms": round(pct(kernel_ms, 10), 5), "p90_ms": round(pct(kernel_ms, 90), 5),
                    "flops_per_launch": flops, "flops_exact_pairs": pairs_exact * fpp,
                    "algorithmic_bytes_per_launch": abytes,
-                   "achieved_TFLOPs": round(flops / (kernel_ms_avg * 1e-3) / 1e12, 2),
+                   "achieved_TFLOPs": tf(kernel_ms_avg),
                    "achieved_GBps_algorithmic": round(abytes / (kernel_ms_avg * 1e-3) / 1e9, 1),
                    "source_hash": src_hash},
     }
-    if split:
-        n_o = out.numel() * out.element_size()
-        n_st = smax.numel() * 4
-        merge_bytes = len(chunks) * (n_o + 2 * n_st) + n_o + 2 * n_st
-        merge_ms = sum(a.elapsed_time(b) for a, b in merge_ev) / len(merge_ev)
+    if run.split:
+        n_o = run.out.numel() * run.out.element_size()
+        n_st = run.smax.numel() * 4
+        merge_bytes = len(run.chunks) * (n_o + 2 * n_st) + n_o + 2 * n_st
+        merge_ms = sum(a.elapsed_time(b) for a, b in run.merge_ev) / len(run.merge_ev)
         result["config"]["key_chunks"] = list(synth.C7_CUTS)
         result["merge_kernel"] = {"avg_ms": round(merge_ms, 5), "bytes_per_launch": merge_bytes,
                                   "achieved_GBps": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1),
                                   "frac_of_hbm": round(merge_bytes / (merge_ms * 1e-3) / 1e9 / HBM_GBPS, 4)}
         result["kernel"]["note"] = "avg_ms covers the forward calls of all key chunks; the merge is timed apart"
-    if args.cold:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cold = []
-        for _ in range(max(5, args.steps // 5)):
-            flush.fill_(1)
-            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            step(ev)
-            torch.cuda.synchronize()
-            cold.append(ev[0].elapsed_time(ev[1]))
-        cold_ms = sorted(cold)[len(cold) // 2]
+    if not args.no_cold:
+        cold = run.cold(max(5, args.steps // 4), dev)
+        cold_ms = pct(cold, 50)
         result["kernel"]["cold_median_ms"] = round(cold_ms, 5)
-        result["kernel"]["cold_tflops"] = round(flops / (cold_ms * 1e-3) / 1e12, 2)
+        result["kernel"]["cold_tflops"] = tf(cold_ms)
+        result["kernel"]["cold_note"] = "one call at a time after writing 512 MiB (the inputs leave the 256 MiB " \
+                                        "last-level cache); the timed steps above run back to back on warm caches"
+    if not args.no_clock:
+        mhz = run.clock_under_load(dev)
+        result["sclk_mhz_under_load"] = round(mhz, 1) if mhz else None
+    if args.workload in DTYPE_WORKLOADS and not args.no_companion:
+        # the same workload in the other 16-bit type, timed the same way
+        other = "fp16" if dtype == "bf16" else "bf16"
+        del run
+        torch.cuda.empty_cache()
+        run2 = Runner(synth.workload(args.workload, other), args.workload, dev)
+        el2, ms2 = run2.timed(args.steps, args.warmup)
+        avg2 = sum(ms2) / len(ms2)
+        result["companion"] = {"dtype": other, "value": round(flops / (el2 / args.steps) / 1e12, 2),
+                               "kernel_avg_ms": round(avg2, 5), "kernel_median_ms": round(pct(ms2, 50), 5),
+                               "achieved_TFLOPs": tf(avg2), "frac": round(tf(avg2) / PEAK_TFLOPS[other], 4),
+                               "plan": run2.desc}
+        del run2
     print(f"[bench] {args.workload} {dtype}: {value:.1f} TFLOP/s, kernel {kernel_ms_avg:.4f} ms avg", file=sys.stderr,
           flush=True)
     if not args.no_cpu_baseline:

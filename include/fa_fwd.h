@@ -205,7 +205,8 @@ fa_status fa_fwd_get_workspace_size(
  * (workspace, workspaceSize, executor, stream).
  *
  * Returns FA_OK, FA_ERR_PARAM_NULLPTR (plan NULL), FA_ERR_WORKSPACE or
- * FA_ERR_RUNTIME.  The plan is not consumed.
+ * FA_ERR_RUNTIME.  The plan is not consumed (see fa_plan_destroy): it may be
+ * executed again, with the same or another workspace of sufficient size.
  */
 fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_plan* plan, void* stream);
 
@@ -240,13 +241,26 @@ fa_status fa_fwd_merge(int32_t n_parts, const fa_tensor* part_out, const fa_tens
                        const char* softmax_out_layout, const fa_tensor* attention_out,
                        const fa_tensor* softmax_max, const fa_tensor* softmax_sum, void* stream);
 
-/* Release a plan from phase 1.  NULL is ignored. */
+/* Release a plan from phase 1.  NULL is ignored.  Passage: V5 page, 调用示例,
+ * which calls the second phase once and then releases the tensors and the
+ * device memory but never the executor; the pages do not say whether the
+ * second phase consumes it.  Here phase 2 does not: a plan may be executed
+ * any number of times (repeated launches on fixed buffers), and the caller
+ * releases it with this call when done.  A plan holds host memory only. */
 void fa_plan_destroy(fa_plan* plan);
 
 /* Text of the chosen kernel, tile and grid, e.g. for logs.  Writes at most
  * `len` bytes including the terminating NUL into `buf`; returns the length
  * the full text needs (excluding NUL), or -1 if plan or buf is NULL. */
 int32_t fa_plan_describe(const fa_plan* plan, char* buf, size_t len);
+
+/* Measurement utility (not part of the forward): enqueue on `stream` one
+ * wavefront that idles for `microseconds` (1..1000000) of the GPU's constant
+ * 100 MHz counter and writes to `device_out` (device memory, two uint64) the
+ * shader-clock cycles and the 100 MHz ticks that passed, so that their ratio
+ * is the shader clock while other work runs beside it.  Returns FA_OK,
+ * FA_ERR_PARAM_NULLPTR, FA_ERR_UNSUPPORTED or FA_ERR_RUNTIME. */
+fa_status fa_clock_probe(uint32_t microseconds, unsigned long long* device_out, void* stream);
 
 /* Reason for the last non-zero status returned on the calling thread
  * (static, thread-local storage; never NULL). */

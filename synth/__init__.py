@@ -180,7 +180,8 @@ def varlen_case(name: str, lengths_q: Sequence[int], nq: int, d: int, dtype: str
 # ---------------------------------------------------------------------------
 
 WORKLOADS = ("c1_fp32_bnsd", "c2_dense_bsnd", "c3_causal", "c3_band", "c4_varlen_causal",
-             "c5_varlen_sink_rope", "c6_dense_pse", "c7_outer_split")
+             "c5_varlen_sink_rope", "c6_dense_pse", "c7_outer_split", "c2_gqa_nkv4", "c2_mqa",
+             "d256_dense_bsnd")
 
 # The c7 workload runs the c2 problem as an outer split: its keys in these
 # chunks, one forward call per chunk (with its kv start), then the merge.
@@ -216,6 +217,16 @@ def workload(name: str, dtype: str = "bf16", small: bool = False) -> Case:
     if name == "c7_outer_split":
         s = 4096 if not small else 320
         return dense_case(name, "BSND", 2, 24 if not small else 3, s, 128, "bf16", seed=2)
+    if name in ("c2_gqa_nkv4", "c2_mqa"):
+        # the headline shape with grouped key / value heads: 24 query heads over 4 or 1 kv heads
+        s = 4096 if not small else 320
+        n = 24 if not small else 4
+        return dense_case(name, "BSND", 2, n, s, 128, dtype, seed=8, nkv=(4 if name == "c2_gqa_nkv4" else 1)
+                          if not small else (2 if name == "c2_gqa_nkv4" else 1))
+    if name == "d256_dense_bsnd":
+        # head dim 256 at the headline's FLOP count: B2 S4096 N12
+        s = 4096 if not small else 320
+        return dense_case(name, "BSND", 2, 12 if not small else 2, s, 256, dtype, seed=9)
     if name == "c6_dense_pse":
         # the additive bias term: a full [B, N, S, S] pse makes the pass HBM-bound
         s = 4096 if not small else 300

@@ -339,6 +339,44 @@ def test_phase2_argument_errors_without_launch():
     _lib.fa_plan_destroy(pl)
 
 
+def test_plan_is_not_consumed_by_phase2():
+    """Phase 2 leaves the plan alive (reusable plans; the caller releases it with fa_plan_destroy):
+    the same plan answers several phase-2 calls and still describes itself afterwards."""
+    L = _lib.lib()
+    q = desc([300, 2, 128])
+    cu = desc([3], I32)
+    st, ws, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND")
+    assert st == 0 and ws > 0
+    before = describe(pl)
+    for _ in range(3):
+        assert L.fa_fwd(ctypes.c_void_p(ADDR), ws - 16, pl, None) == 561201  # returns before any launch
+    assert describe(pl) == before
+    _lib.fa_plan_destroy(pl)
+    header = open(HEADER).read()
+    assert "The plan is not consumed" in header and "调用示例" in header
+
+
+def test_clock_probe_argument_errors_without_launch():
+    L = _lib.lib()
+    assert L.fa_clock_probe(1000, None, None) == 161001
+    assert L.fa_clock_probe(0, ctypes.c_void_p(ADDR), None) == 561103
+    assert L.fa_clock_probe(1000001, ctypes.c_void_p(ADDR), None) == 561103
+
+
+def test_fa_log_prints_the_plan(monkeypatch, capfd):
+    q, k, v, o = c2()
+    monkeypatch.setenv("FA_LOG", "1")
+    st, _, pl = plan(q, k, v, o)
+    assert st == 0
+    _lib.fa_plan_destroy(pl)
+    err = capfd.readouterr().err
+    assert "[fa_fwd] plan kernel=mfma_pp " in err and "layout=BSND" in err, err
+    monkeypatch.setenv("FA_LOG", "0")
+    st, _, pl = plan(q, k, v, o)
+    _lib.fa_plan_destroy(pl)
+    assert "[fa_fwd]" not in capfd.readouterr().err
+
+
 def test_plan_destroy_null_and_describe_null():
     L = _lib.lib()
     L.fa_plan_destroy(None)
@@ -505,7 +543,7 @@ def test_d96_on_matrix_cores(dr, monkeypatch):
     _lib.fa_plan_destroy(pl)
     monkeypatch.setenv("FA_FWD_KERNEL", "pp")  # the two-group kernel has no D = 96
     st, _, pl = plan(desc(s), desc(s), desc(s), desc(s), **kw)
-    assert st == 561103 and pl is None and "D = 64 and 128" in _lib.last_error_message()
+    assert st == 561103 and pl is None and "D = Dv = 64 or 128" in _lib.last_error_message()
 
 
 @pytest.mark.parametrize("dqk,dv,want", [(192, 128, "d=128 dr=64"), (128, 64, "d=64 dr=64"), (160, 96, "d=96 dr=64")])
@@ -521,6 +559,26 @@ def test_dqk_above_dv_on_matrix_cores(dqk, dv, want):
     st, ws, pl = plan(q, q, v, v, pse=desc([1, 4, 512, 512]), layout=b"BSND")
     assert st == 0 and "kernel=generic" in describe(pl) and f"d={dqk} dr=0" in describe(pl), describe(pl)
     _lib.fa_plan_destroy(pl)
+
+
+@pytest.mark.parametrize("dv", [256, 128])
+def test_d256_on_matrix_cores(dv, monkeypatch):
+    # head dim 256 (the largest the aclnnFlashAttentionScore page lists) runs the four-wave kernel, one
+    # workgroup per CU (its two LDS stages take 128 KiB); Dv = 256 or 128
+    q, v = desc([2, 4096, 16, 256]), desc([2, 4096, 16, dv])
+    st, ws, pl = plan(q, q, v, v)
+    assert st == 0, _lib.last_error_message()
+    d = describe(pl)
+    assert "kernel=mfma " in d and "d=256 dr=0 " in d and f"dv={dv} " in d and "kv_splits=1" in d, d
+    _lib.fa_plan_destroy(pl)
+    # a small grid splits the keys against one workgroup slot per CU: 16 tiles x 2 heads = 32 workgroups
+    q2, v2 = desc([1, 2048, 2, 256]), desc([1, 2048, 2, dv])
+    st, ws, pl = plan(q2, q2, v2, v2)
+    assert st == 0 and "kv_splits=4" in describe(pl) and ws > 0, describe(pl)
+    _lib.fa_plan_destroy(pl)
+    monkeypatch.setenv("FA_FWD_KERNEL", "pp")
+    st, _, pl = plan(q, q, v, v)
+    assert st == 561103 and pl is None and "two-group" in _lib.last_error_message()
 
 
 def test_small_grid_uses_four_wave_kernel():

@@ -44,6 +44,9 @@ SMALL = {
     "c3_small_band": lambda: synth.workload("c3_band", small=True),
     "c4_small_varlen": lambda: synth.workload("c4_varlen_causal", small=True),
     "c5_small_sink_rope": lambda: synth.workload("c5_varlen_sink_rope", small=True),
+    "c2_small_gqa_nkv4": lambda: synth.workload("c2_gqa_nkv4", small=True),
+    "c2_small_mqa_fp16": lambda: synth.workload("c2_mqa", "fp16", small=True),
+    "d256_small_dense": lambda: synth.workload("d256_dense_bsnd", small=True),
     "bnsd_ragged_201": lambda: synth.dense_case("x", "BNSD", 2, 2, 201, 128, "bf16", 31),
     "bsnd_d64": lambda: synth.dense_case("x", "BSND", 1, 3, 190, 64, "bf16", 32),
     "bsnd_d64_rope": lambda: synth.dense_case("x", "BSND", 1, 2, 150, 64, "bf16", 33, drope=64, causal=True),
@@ -513,7 +516,8 @@ def test_v5_call_example_on_gpu():
 # full-size workloads, sampled rows
 # ---------------------------------------------------------------------------
 
-FULL = ["c2_bf16", "c2_fp16", "c3_causal", "c3_band", "c4_varlen_causal", "c5_varlen_sink_rope", "c6_dense_pse"]
+FULL = ["c2_bf16", "c2_fp16", "c3_causal", "c3_band", "c4_varlen_causal", "c5_varlen_sink_rope", "c6_dense_pse",
+        "c2_gqa_nkv4", "c2_mqa", "d256_dense_bsnd"]
 
 
 def _full_case(name):
