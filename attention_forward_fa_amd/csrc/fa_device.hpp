@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "fa_params.h"
+#include "fa_tilemap.h"
 
 namespace fa {
 
@@ -90,12 +91,6 @@ __device__ __forceinline__ Tile map_tile(const Params& p, int bid) {
   return t;
 }
 
-// Rows of a sequence clamped the same way map_tile clamps them.
-__device__ __forceinline__ int seq_rows(const int32_t* cu, int b, int total) {
-  const int a = min(max(cu[b], 0), total);
-  const int e = min(max(cu[b + 1], a), total);
-  return e - a;
-}
 
 // Key range [lo, hi] any row of [i_first, i_last] may keep (window and length).
 __device__ __forceinline__ void key_range(const Params& p, int i_first, int i_last, int skv, int* lo, int* hi) {

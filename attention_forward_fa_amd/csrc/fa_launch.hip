@@ -17,7 +17,7 @@ __global__ void __launch_bounds__(256) varlen_tile_prefix(const int32_t* __restr
   const int per = (nbatch + 255) / 256;
   const int b0 = min(tid * per, nbatch), b1 = min(b0 + per, nbatch);
   int s = 0;
-  for (int b = b0; b < b1; ++b) s += (seq_rows(cu, b, total) + bm - 1) / bm;
+  for (int b = b0; b < b1; ++b) s += seq_tiles(cu, b, total, bm);
   part[tid] = s;
   __syncthreads();
   if (tid == 0) {
@@ -32,7 +32,7 @@ __global__ void __launch_bounds__(256) varlen_tile_prefix(const int32_t* __restr
   int acc = part[tid];
   for (int b = b0; b < b1; ++b) {
     prefix[b] = acc;
-    acc += (seq_rows(cu, b, total) + bm - 1) / bm;
+    acc += seq_tiles(cu, b, total, bm);
   }
   if (b1 == nbatch && b0 < b1) prefix[nbatch] = acc;
   if (nbatch == 0 && tid == 0) prefix[0] = 0;
@@ -42,27 +42,11 @@ __global__ void __launch_bounds__(256) varlen_tile_prefix(const int32_t* __restr
   // the sequence b, its query tile qt and the clamped row / key ranges of the
   // tile it runs; heavier (later) tiles first when `reverse`.  Entries past
   // the total are marked invalid.
-  const int ntiles = prefix[nbatch];
-  const int tq = total;
-  const int32_t* cu_q = cu;
   for (int r = threadIdx.x; r < tph; r += 256) {
-    int4 e0 = make_int4(0, 0, 0, 0), e1 = make_int4(0, 0, 0, 0);
-    if (r < ntiles) {
-      const int rr = reverse ? ntiles - 1 - r : r;
-      // largest b with prefix[b] <= rr (prefix is non-decreasing, prefix[0] = 0)
-      int lo = 0, hi = nbatch - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (prefix[mid] <= rr) lo = mid; else hi = mid - 1;
-      }
-      // clamped so a corrupt cu_seqlens can only shrink the work, never reach outside [0, T)
-      const int q0 = min(max(cu_q[lo], 0), tq), q1 = min(max(cu_q[lo + 1], q0), tq);
-      const int k0 = min(max(cu_kv[lo], 0), tkv), k1 = min(max(cu_kv[lo + 1], k0), tkv);
-      e0 = make_int4(lo, rr - prefix[lo], q0, k0);
-      e1 = make_int4(q1 - q0, k1 - k0, 1, 0);
-    }
-    reinterpret_cast<int4*>(map)[2 * r] = e0;
-    reinterpret_cast<int4*>(map)[2 * r + 1] = e1;
+    int32_t e[8];
+    tile_entry(prefix, cu, cu_kv, nbatch, total, tkv, reverse, r, e);
+    reinterpret_cast<int4*>(map)[2 * r] = make_int4(e[0], e[1], e[2], e[3]);
+    reinterpret_cast<int4*>(map)[2 * r + 1] = make_int4(e[4], e[5], e[6], e[7]);
   }
 }
 

@@ -14,6 +14,7 @@ from __future__ import annotations
 import contextlib
 import math
 import os
+import time
 from typing import Dict, Optional
 
 import torch
@@ -38,6 +39,25 @@ def forced_kernel(kind: str):
             os.environ.pop("FA_FWD_KERNEL", None)
         else:
             os.environ["FA_FWD_KERNEL"] = old
+
+
+# Stream watchdog: the GPU work a test enqueues must finish within this many
+# seconds, else the test fails with a TimeoutError naming what it waited for
+# (instead of blocking the whole run inside a synchronize).
+GPU_DEADLINE_S = float(os.environ.get("FA_TEST_GPU_DEADLINE_S", "120"))
+
+
+def sync_with_deadline(what: str = "GPU work", seconds: Optional[float] = None) -> None:
+    """Wait for everything enqueued on the current stream, polling an event, up to a deadline."""
+    limit = GPU_DEADLINE_S if seconds is None else seconds
+    ev = torch.cuda.Event()
+    ev.record()
+    t0 = time.monotonic()
+    while not ev.query():
+        if time.monotonic() - t0 > limit:
+            raise TimeoutError(f"{what} did not finish within {limit:.0f} s")
+        time.sleep(0.0005)
+    torch.cuda.synchronize()
 
 
 def to_gpu(t: Optional[torch.Tensor], dev="cuda:0"):
@@ -70,7 +90,7 @@ def run_gpu_poisoned(case: synth.Case, dev="cuda:0"):
                            real_shift=g["pse"])
     try:
         plan.run()
-        torch.cuda.synchronize()
+        sync_with_deadline(f"forward on {case.layout} q={tuple(case.q.shape)}")
     finally:
         plan.close()
     return out.cpu(), smax.cpu(), ssum.cpu()
@@ -91,7 +111,7 @@ def run_gpu(case: synth.Case, *, stats: bool = True, layout_heads: Optional[int]
             heads=layout_heads, pre_tokens=case.pre_tokens, next_tokens=case.next_tokens, sink=g["sink"],
             query_rope=g["q_rope"], key_rope=g["k_rope"], causal=case.causal, pse=g["pse"],
             return_softmax_stats=stats)
-    torch.cuda.synchronize()
+    sync_with_deadline(f"forward on {case.layout} q={tuple(case.q.shape)}")
     if stats:
         return tuple(x.cpu() for x in res)
     return res.cpu(), None, None

@@ -451,6 +451,31 @@ def test_guard_bands_untouched():
     plan.close()
 
 
+def test_guard_bands_malformed_cu_seqlens():
+    """cu_seqlens that decrease and run past T: phase 2 clamps each sequence into [0, T), so the
+    kernels write nothing outside O and the statistics (the rows the clamped sequences cover are
+    written, the bands around the buffers stay as they were)."""
+    T, N, D = 577, 2, 128
+    g = synth.generator(130)
+    q, k, v = (synth.normal((T, N, D), g, "bf16").cuda() for _ in range(3))
+    cu = torch.tensor([0, 300, 200, 700], dtype=torch.int32, device="cuda")  # covers [0, 300) and [200, 577)
+    pad, poison = 4096, -12345.0
+    obuf = torch.full((pad + T * N * D + pad,), poison, dtype=torch.bfloat16, device="cuda")
+    out = obuf[pad:pad + T * N * D].view(T, N, D)
+    sbuf = torch.full((pad + N * T * 8 + pad,), poison, dtype=torch.float32, device="cuda")
+    smax = sbuf[pad:pad + N * T * 8].view(N, T, 8)
+    print("[parity] start guard bands, malformed cu_seqlens [0, 300, 200, 700] T=577", flush=True)
+    plan = api.ForwardPlan(q, k, v, layout="TND", scale=D ** -0.5, head_num=N, cu_seqlens_q=cu, cu_seqlens_kv=cu,
+                           causal=True, out=out, softmax_max=smax, softmax_sum=None)
+    plan.run()
+    pu.sync_with_deadline("forward with malformed cu_seqlens")
+    plan.close()
+    for buf in (obuf, sbuf):
+        assert bool((buf[:pad] == poison).all()) and bool((buf[-pad:] == poison).all())
+    assert not bool((out == poison).any()) and not bool((smax == poison).any())
+    assert bool(torch.isfinite(out.float()).all())
+
+
 def test_key_split_guard_bands_untouched(monkeypatch):
     """The split writes only its workspace and, through the merge, exactly the output and statistics rows."""
     monkeypatch.setenv("FA_FWD_KV_SPLIT", "3")
