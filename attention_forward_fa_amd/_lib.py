@@ -36,7 +36,7 @@ FA_DTYPE = {
 }
 
 EXPORTED = ("fa_fwd_get_workspace_size", "fa_fwd", "fa_fwd_merge", "fa_plan_destroy", "fa_plan_describe",
-            "fa_last_error_message", "fa_clock_probe")
+            "fa_last_error_message", "fa_clock_probe", "fa_fwd_noalloc")
 
 
 class FaTensor(ctypes.Structure):
@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_merge.restype = ctypes.c_int32
         L.fa_fwd_merge.argtypes = [ctypes.c_int32, T, T, T, ctypes.c_char_p, ctypes.c_int64, ctypes.c_char_p,
                                    T, T, T, ctypes.c_void_p]
+        L.fa_fwd_noalloc.restype = ctypes.c_int32
+        L.fa_fwd_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.fa_clock_probe.restype = ctypes.c_int32
         L.fa_clock_probe.argtypes = [ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
         L.fa_last_error_message.restype = ctypes.c_char_p
@@ -163,6 +165,13 @@ def fa_fwd(workspace: Optional[torch.Tensor], workspace_size: int, plan, stream:
     st = L.fa_fwd(ptr, int(workspace_size), plan, stream)
     if st != FA_OK:
         raise FaError(st, "fa_fwd", last_error_message())
+
+
+def fa_fwd_noalloc(plan, stream: int) -> None:
+    """Phase 2 with the library's own scratch array instead of a workspace (allocates nothing)."""
+    st = lib().fa_fwd_noalloc(plan, stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_noalloc", last_error_message())
 
 
 def fa_fwd_merge(part_out, part_max, part_sum, input_layout: str, head_num: int, softmax_out_layout: str,

@@ -1,6 +1,8 @@
 // Phase 2 of the two-phase forward: enqueue the planned kernels on a stream.
 #include <stdio.h>
 
+#include <mutex>
+
 #include "fa_launch.h"
 #include "fa_plan.h"
 #include "fa_device.hpp"
@@ -169,23 +171,12 @@ fa_status runtime_fail(const char* what, hipError_t e) {
 
 }  // namespace
 
-extern "C" fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_plan* plan, void* stream) {
-  if (!plan) {
-    fa_set_error("plan is NULL");
-    return FA_ERR_PARAM_NULLPTR;
-  }
-  if (plan->ws_bytes > 0 && (!workspace || workspace_size < plan->ws_bytes)) {
-    char buf[128];
-    snprintf(buf, sizeof(buf), "workspace needs %llu bytes, got %llu at %p", (unsigned long long)plan->ws_bytes,
-             (unsigned long long)workspace_size, workspace);
-    fa_set_error(buf);
-    return FA_ERR_WORKSPACE;
-  }
+namespace {
+
+// Enqueue the planned kernels with `workspace` (at least plan->ws_bytes,
+// 16-byte aligned, or unused when that is 0) as their scratch memory.
+fa_status enqueue(const fa_plan* plan, void* workspace, void* stream) {
   fa::Params p = plan->p;
-  if (plan->ws_bytes > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15u)) {
-    fa_set_error("workspace must be 16-byte aligned");
-    return FA_ERR_WORKSPACE;
-  }
   if (p.num_wg == 0) return FA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.has_mask && plan->kind != fa::KERNEL_GENERIC) {  // the generic kernel reads the mask everywhere
@@ -243,6 +234,85 @@ extern "C" fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_p
     if (e != hipSuccess) return runtime_fail("key split merge launch", e);
   }
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_plan* plan, void* stream) {
+  if (!plan) {
+    fa_set_error("plan is NULL");
+    return FA_ERR_PARAM_NULLPTR;
+  }
+  if (plan->ws_bytes > 0 && (!workspace || workspace_size < plan->ws_bytes)) {
+    char buf[128];
+    snprintf(buf, sizeof(buf), "workspace needs %llu bytes, got %llu at %p", (unsigned long long)plan->ws_bytes,
+             (unsigned long long)workspace_size, workspace);
+    fa_set_error(buf);
+    return FA_ERR_WORKSPACE;
+  }
+  if (plan->ws_bytes > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15u)) {
+    fa_set_error("workspace must be 16-byte aligned");
+    return FA_ERR_WORKSPACE;
+  }
+  return enqueue(plan, workspace, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing: the library's own scratch array
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// Device scratch for fa_fwd_noalloc, one copy per GPU the library runs on,
+// held until the process ends.  On the host this name is only a stand-in for
+// the symbol: its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch`, looked up once per device (with that
+// device current, as it is for the caller's stream).
+fa_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return runtime_fail("hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices) {
+    fa_set_error("device index beyond the scratch table");
+    return FA_ERR_RUNTIME;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return runtime_fail("hipGetSymbolAddress(scratch)", e);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" fa_status fa_fwd_noalloc(const fa_plan* plan, void* stream) {
+  if (!plan) {
+    fa_set_error("plan is NULL");
+    return FA_ERR_PARAM_NULLPTR;
+  }
+  if (plan->ws_bytes > FA_NOALLOC_SCRATCH_BYTES) {
+    char buf[160];
+    snprintf(buf, sizeof(buf), "plan needs %llu bytes of scratch, above the %llu the no-allocation entry point holds",
+             (unsigned long long)plan->ws_bytes, (unsigned long long)FA_NOALLOC_SCRATCH_BYTES);
+    fa_set_error(buf);
+    return FA_ERR_UNSUPPORTED;
+  }
+  void* ws = nullptr;
+  if (plan->ws_bytes > 0) {
+    const fa_status st = scratch_for_current_device(&ws);
+    if (st != FA_OK) return st;
+  }
+  return enqueue(plan, ws, stream);
 }
 
 extern "C" fa_status fa_clock_probe(uint32_t microseconds, unsigned long long* device_out, void* stream) {

@@ -211,6 +211,26 @@ fa_status fa_fwd_get_workspace_size(
 fa_status fa_fwd(void* workspace, uint64_t workspace_size, const fa_plan* plan, void* stream);
 
 /*
+ * Phase 2 for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same work as
+ * fa_fwd, with the library's own device scratch array (one per GPU, of
+ * FA_NOALLOC_SCRATCH_BYTES, held until the process ends) in place of the
+ * caller's workspace.  It allocates and frees nothing.  The array's device
+ * address is looked up once per device on that device's first call.
+ *
+ * Every call on one GPU shares that GPU's array: calls whose device work may
+ * overlap (on different streams, or on one stream from several threads
+ * without ordering) race on it and must not be issued.  Nothing in the
+ * array needs to start at zero; it keeps the last call's contents.
+ *
+ * Returns FA_OK, FA_ERR_PARAM_NULLPTR (plan NULL), FA_ERR_UNSUPPORTED (the
+ * plan's workspace size, from phase 1, is above FA_NOALLOC_SCRATCH_BYTES) or
+ * FA_ERR_RUNTIME.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32ull << 20)
+fa_status fa_fwd_noalloc(const fa_plan* plan, void* stream);
+
+/*
  * Merge the results of one query chunk computed against several key chunks
  * (an outer split along the key sequence: one fa_fwd call per chunk with its
  * kv_start_idx, the sink given to one call only) into the result over all

@@ -17,6 +17,11 @@ extern "C" fa_status fa_fwd(void*, uint64_t, const fa_plan*, void*) {
   return FA_ERR_RUNTIME;
 }
 
+extern "C" fa_status fa_fwd_noalloc(const fa_plan*, void*) {
+  fa_set_error("host-only build: no device");
+  return FA_ERR_RUNTIME;
+}
+
 extern "C" fa_status fa_clock_probe(uint32_t, unsigned long long*, void*) {
   fa_set_error("host-only build: no device");
   return FA_ERR_RUNTIME;

@@ -377,6 +377,19 @@ def test_fa_log_prints_the_plan(monkeypatch, capfd):
     assert "[fa_fwd]" not in capfd.readouterr().err
 
 
+def test_noalloc_argument_errors_without_launch():
+    L = _lib.lib()
+    assert L.fa_fwd_noalloc(None, None) == 161001
+    # B1 N8 S4096 D128: the small grid splits its keys in two, whose fp32 partials need more scratch
+    # than the no-allocation entry point holds (32 MiB): refused before any device call
+    s = [1, 8, 4096, 128]
+    st, ws, pl = plan(desc(s), desc(s), desc(s), desc(s), layout=b"BNSD")
+    assert st == 0 and ws > (32 << 20), describe(pl)
+    assert L.fa_fwd_noalloc(ctypes.c_void_p(pl), None) == 561103
+    assert "scratch" in _lib.last_error_message()
+    _lib.fa_plan_destroy(pl)
+
+
 def test_plan_destroy_null_and_describe_null():
     L = _lib.lib()
     L.fa_plan_destroy(None)

@@ -18,7 +18,7 @@ CSRC = os.path.join(ROOT, "attention_forward_fa_amd", "csrc")
 OUT = os.path.join(ROOT, "_build", "asan")
 
 # tests that need the device half (phase 2, the clock probe) or the full export list are left out
-DESELECT = "not phase2 and not not_consumed and not clock_probe and not header_symbols"
+DESELECT = "not phase2 and not not_consumed and not clock_probe and not header_symbols and not noalloc"
 
 
 def _asan_runtime():
