@@ -15,8 +15,11 @@
 //
 // and the groups are offset by one phase, with a workgroup barrier between
 // phases: while group 0 issues matrix instructions, group 1 does its softmax,
-// then they swap.  The M phase runs at raised wave priority, and its LDS
-// operand reads are issued four MFMAs ahead of their use.
+// then they swap.  The M phase runs at raised wave priority; its LDS operand
+// reads are issued four MFMAs ahead of their use, two MFMAs' reads at a time,
+// so that one wait covers a pair of MFMAs.  Steps whose blocks are full for
+// both groups (no window edge, sequence end or mask) run without the
+// per-block tests.
 //
 // K and V: NSLOT slots, block b in slot b % NSLOT.  In step b each group
 // loads its share of block b + NSLOT - 1 during its M phase, the loads spread
@@ -148,11 +151,27 @@ __device__ __forceinline__ void pp_scores(const char* __restrict__ slot, const P
 // LDS operand reads run this many MFMAs ahead in the M phase.
 constexpr int kPpAhead = 4;
 
+// s_waitcnt lgkmcnt(n) (n <= 8), vector memory and export counters untouched.
+__device__ __forceinline__ void pp_wait_lgkm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0xc07f); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0xc17f); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0xc27f); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0xc37f); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0xc47f); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0xc57f); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0xc67f); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0xc77f); break;
+    default: __builtin_amdgcn_s_waitcnt(0xc87f); break;
+  }
+}
+
 // The M phase as one stream of MFMAs: the score MFMAs of the block in kslot
 // (when do_s), then the P V MFMAs of the block in vslot (when do_pv), with
 // every LDS operand read issued kPpAhead MFMAs ahead of its use (the
 // sched_group_barrier sequence keeps the compiler from pulling them back),
-// then this wave's loads of the block at jfill into slot fill.
+// and this wave's loads of the block at jfill into slot fill spread between
+// them.
 template <typename T, int D, int DR>
 __device__ __forceinline__ void pp_mphase(const char* __restrict__ kslot, const char* __restrict__ vslot,
                                           char* __restrict__ fill, int jfill, bool do_s, bool do_pv,
@@ -188,36 +207,59 @@ __device__ __forceinline__ void pp_mphase(const char* __restrict__ kslot, const 
     return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   if (do_s && do_pv) {
-    V8 a[NS + NP];
-#pragma unroll
-    for (int i = 0; i < NS + NP + kPpAhead; ++i) {
-      if (i < NS) a[i] = kread(i);
-      else if (i < NS + NP) a[i] = vread(i - NS);
-      const int j = i - kPpAhead;
-      if (j >= 0 && j < NS) {
+    // MFMAs in pairs: the operand reads of a pair are issued together,
+    // kPpAhead MFMAs ahead, so one LDS wait covers both MFMAs of a pair
+    constexpr int NM = NS + NP;
+    static_assert(NM % 2 == 0 && kPpAhead % 2 == 0, "pairs");
+    auto ops = [](int m) { return m < NS ? 1 : 2; };  // LDS instructions of MFMA m's operand
+    V8 a[NM];
+    auto issue_read = [&](int m) {
+      if (m < NS) a[m] = kread(m);
+      else if (m < NM) a[m] = vread(m - NS);
+    };
+    auto issue_mfma = [&](int j) {
+      if (j < NS) {
         s[j & 1] = mfma32<T>(a[j], qf[j >> 1], j < 2 ? f32x16{} : s[j & 1]);
-      } else if (j >= NS) {
+      } else {
         const int q = j - NS, ts = q / C::NDT;
         oacc[q % C::NDT] = mfma32<T>(a[j], pk[ts >> 1][ts & 1], oacc[q % C::NDT]);
       }
-      // the next block's loads, spread evenly between the MFMAs
+    };
+#pragma unroll
+    for (int m = 0; m < kPpAhead; ++m) issue_read(m);
+#pragma unroll
+    for (int j = 0; j < NM; j += 2) {
+      int outstanding = 0;  // reads of MFMAs j + 2 .. j + kPpAhead - 1 may still fly
+#pragma unroll
+      for (int m = j + 2; m < j + kPpAhead && m < NM; ++m) outstanding += ops(m);
+      pp_wait_lgkm(outstanding);
+      issue_mfma(j);
+      issue_mfma(j + 1);
+      issue_read(j + kPpAhead);
+      issue_read(j + kPpAhead + 1);
+      // the next block's loads, spread evenly between the MFMA pairs
 #pragma unroll
       for (int n = 0; n < C::LPB; ++n)
-        if (j == (n + 1) * (NS + NP) / (C::LPB + 1)) pp_stage_one<T, D, DR>(fill, jfill, x, n);
+        if (j / 2 == (n + 1) * (NM / 2) / (C::LPB + 1)) pp_stage_one<T, D, DR>(fill, jfill, x, n);
     }
-    // keep the reads kPpAhead MFMAs ahead (the scheduler would pull them back)
-    __builtin_amdgcn_sched_group_barrier(0x100, kPpAhead, 0);
+    // the same order for the scheduler: first reads, then per pair two
+    // MFMAs, the next pair's reads and any load
+    if (kPpAhead == 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int j = 0; j < NS + NP; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    for (int j = 0; j < NM; j += 2) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       const int n = j + kPpAhead;
-      if (n < NS)
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      else if (n < NS + NP)
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (n < NM) {
+        if (ops(n) + ops(n + 1) == 2)
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else if (ops(n) + ops(n + 1) == 3)
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
 #pragma unroll
       for (int m = 0; m < C::LPB; ++m)
-        if (j == (m + 1) * (NS + NP) / (C::LPB + 1)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        if (j / 2 == (m + 1) * (NM / 2) / (C::LPB + 1)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     }
     return;
   }
@@ -262,13 +304,13 @@ __device__ __forceinline__ uint32_t pp_mask_word(const Params& p, const PpCtx<T>
 // Softmax step of the block at jb (scores in st.sacc) -> st.pk.  Blocks that
 // cross the window edge or the sequence end, or whose mask block is mixed,
 // first set their excluded scores to -inf.
-template <typename T, int D, int DR>
+template <typename T, int D, int DR, bool FULL = false>
 __device__ __forceinline__ void pp_softmax(const Params& p, const PpCtx<T>& x, int jb, PpState<T, D, DR>& st) {
   using C = PpCfg<T, D, DR>;
   constexpr int BN = C::BN;
-  const bool tail = jb + BN > x.skv;
-  const bool edge = p.band && !(jb >= x.g_last - p.pre && jb + BN - 1 <= x.g_first + p.next);
-  const bool rmask = mask_class(p, x.cls_row, jb) == CLS_MIXED;
+  const bool tail = !FULL && jb + BN > x.skv;
+  const bool edge = !FULL && p.band && !(jb >= x.g_last - p.pre && jb + BN - 1 <= x.g_first + p.next);
+  const bool rmask = !FULL && mask_class(p, x.cls_row, jb) == CLS_MIXED;
   if (tail || edge || rmask) {
     // the row keeps keys [lo, hi]; element (t, a, b) is key jb + 4hh + 32t +
     // 8a + b, kept iff unsigned(b0 + 32t + 8a + b) <= span with b0 = jb + 4hh - lo
@@ -337,10 +379,11 @@ __device__ __forceinline__ void pp_softmax(const Params& p, const PpCtx<T>& x, i
 // k + NSLOT - 1.  The three pointers are
 // restrict-qualified, so the compiler knows the operand reads do not depend
 // on the loads in flight.
-template <typename T, int D, int DR>
+template <typename T, int D, int DR, bool FAST = false>
 __device__ __forceinline__ void pp_step(char* __restrict__ fill, const char* __restrict__ cur,
                                         const char* __restrict__ nxt, int k, int jb0, bool act_k, bool act_k1,
                                         int grp, const Params& p, const PpCtx<T>& x, PpState<T, D, DR>& st) {
+  if (FAST) act_k = act_k1 = true;
   using C = PpCfg<T, D, DR>;
   constexpr int BN = C::BN;
   const int jfill = jb0 + (k + C::NSLOT - 1) * BN;
@@ -350,13 +393,13 @@ __device__ __forceinline__ void pp_step(char* __restrict__ fill, const char* __r
     pp_mphase<T, D, DR>(nxt, cur, fill, jfill, act_k1, act_k, x, st.qf, st.pk, st.sacc, st.oacc);
     __builtin_amdgcn_s_setprio(0);
   } else {
-    if (k == 0 && act_k) pp_scores<T, D, DR>(cur, x, st.qf, st.sacc);
-    if (act_k) pp_softmax<T, D, DR>(p, x, jb0 + k * BN, st);
+    if (!FAST && k == 0 && act_k) pp_scores<T, D, DR>(cur, x, st.qf, st.sacc);
+    if (act_k) pp_softmax<T, D, DR, FAST>(p, x, jb0 + k * BN, st);
   }
   __builtin_amdgcn_s_barrier();
   // phase 2k + 1: group 0 = softmax of block k + 1, group 1 = M phase of step k
   if (grp == 0) {
-    if (act_k1) pp_softmax<T, D, DR>(p, x, jb0 + (k + 1) * BN, st);
+    if (act_k1) pp_softmax<T, D, DR, FAST>(p, x, jb0 + (k + 1) * BN, st);
   } else {
     __builtin_amdgcn_s_setprio(1);
     pp_mphase<T, D, DR>(nxt, cur, fill, jfill, act_k1, act_k, x, st.qf, st.pk, st.sacc, st.oacc);
@@ -490,11 +533,40 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
   }
 
   // ---- main loop
-  for (int k = 0; k < nblocks; ++k) {
-    pp_step<T, D, DR>(slot(k + NSLOT - 1), slot(k), slot(k + 1), k, jb0, active(k), active(k + 1), grp, p, x, st);
+  // Steps whose two blocks are full for both groups (inside every row's
+  // window, before the sequence end, no mask) skip the per-block tests:
+  // blocks [f0, f1] of the workgroup's range are full.  Everything here is
+  // uniform over the workgroup, so both groups run the same steps.
+  int f0 = 1, f1 = 0;
+  if (DR == 0 && !p.has_mask && wg_last >= i0 + 128) {
+    int lo = 0, end = tl.skv;  // full blocks cover keys [lo, end) for both groups
+    if (p.band) {
+      lo = max(lo, wg_last - p.pre);
+      end = min(end, i0 + p.next + 1);
+    }
+    f0 = max(0, (lo - jb0 + BN - 1) / BN);
+    f1 = min(nblocks - 1, (end - jb0) / BN - 1);
+  }
+  const int fa = max(f0, 1), fb = f1;  // fast steps k with blocks k and k + 1 in [f0, f1], k >= 1
+  int k = 0;
+  auto step_end = [&]() {
     // block k + 2 has landed (all but the newest NSLOT - 3 blocks)
     __builtin_amdgcn_s_waitcnt(0x0f70 | ((NSLOT - 3) * C::LPB));
     __builtin_amdgcn_s_barrier();
+  };
+  for (; k < nblocks && !(k >= fa && k < fb); ++k) {
+    pp_step<T, D, DR>(slot(k + NSLOT - 1), slot(k), slot(k + 1), k, jb0, active(k), active(k + 1), grp, p, x, st);
+    step_end();
+  }
+  if constexpr (DR == 0) {
+    for (; k < fb; ++k) {
+      pp_step<T, D, DR, true>(slot(k + NSLOT - 1), slot(k), slot(k + 1), k, jb0, true, true, grp, p, x, st);
+      step_end();
+    }
+  }
+  for (; k < nblocks; ++k) {
+    pp_step<T, D, DR>(slot(k + NSLOT - 1), slot(k), slot(k + 1), k, jb0, active(k), active(k + 1), grp, p, x, st);
+    step_end();
   }
 
   float& m_ref = st.m_ref;
