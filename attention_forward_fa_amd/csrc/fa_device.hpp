@@ -53,6 +53,75 @@ __device__ __forceinline__ int xcd_linear_id(int bid, int grid) {
   return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active), with
+// DPP: shifts by 1, 2, 4 and 8 within each row of 16 lanes, then lane 15 of
+// a row into the next row and lane 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 (rows 1, 3)
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 (rows 2, 3)
+  return v;
+}
+
+// Entry r of the per-head TND tile list found from cu_seqlens, with no tile
+// map: the same entry tile_entry reads from the prefix of seq_tiles
+// (sequence b holds entries [prefix[b], prefix[b + 1]), later entries first
+// when reverse_tiles).  Every wave loads the cumulative lengths of up to
+// kTileSearchMaxSeqs sequences at once, lane i taking sequences i, i + 64,
+// ...; per 64-sequence chunk an inclusive scan gives each sequence's first
+// entry, and the one lane whose entries hold the target reports its
+// sequence, tile and row spans (read into scalar registers).  Called by all
+// threads of the workgroup with full waves; every value it branches on is
+// wave-uniform.  Returns false past the last tile.
+__device__ __forceinline__ bool search_tile(const Params& p, int r, Tile* t) {
+  constexpr int NC = kTileSearchMaxSeqs / 64;
+  const int lane = threadIdx.x & 63;
+  const int nb = p.nbatch;
+  int n[NC], incl[NC], q0[NC], q1[NC], k0[NC], k1[NC], tot[NC];
+  int total = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int b = 64 * c + lane;
+    int qa = 0, qe = 0, ka = 0, ke = 0;
+    if (b < nb) {
+      qa = p.cu_q[b];
+      qe = p.cu_q[b + 1];
+      ka = p.cu_kv[b];
+      ke = p.cu_kv[b + 1];
+    }
+    clamp_span(qa, qe, p.tq, &q0[c], &q1[c]);
+    clamp_span(ka, ke, p.tkv, &k0[c], &k1[c]);
+    n[c] = b < nb ? (q1[c] - q0[c] + p.tile_bm - 1) / p.tile_bm : 0;
+    incl[c] = 64 * c < nb ? wave_incl_scan(n[c]) : 0;
+    tot[c] = __builtin_amdgcn_readlane(incl[c], 63);
+    total += tot[c];
+  }
+  if (r >= total) return false;
+  const int rr = p.reverse_tiles ? total - 1 - r : r;
+  int base = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int first = base + incl[c] - n[c];
+    const unsigned long long hit = __ballot(n[c] > 0 && first <= rr && rr < first + n[c]);
+    if (hit != 0ull) {
+      const int l = __ffsll((long long)hit) - 1;
+      const int a = __builtin_amdgcn_readlane(q0[c], l), ka = __builtin_amdgcn_readlane(k0[c], l);
+      t->b = 64 * c + l;
+      t->qt = rr - __builtin_amdgcn_readlane(first, l);
+      t->q_row0 = a;
+      t->kv_row0 = ka;
+      t->sq = __builtin_amdgcn_readlane(q1[c], l) - a;
+      t->skv = __builtin_amdgcn_readlane(k1[c], l) - ka;
+      return true;
+    }
+    base += tot[c];
+  }
+  return false;
+}
+
 __device__ __forceinline__ Tile map_tile(const Params& p, int bid) {
   Tile t;
   const int lin = xcd_linear_id(bid, p.num_wg);
@@ -78,6 +147,12 @@ __device__ __forceinline__ Tile map_tile(const Params& p, int bid) {
   t.h = lin / tph;
   t.split = 0;
   const int r = lin - t.h * tph;
+  if (p.tile_search) {
+    t.b = t.qt = t.sq = t.skv = 0;
+    t.q_row0 = t.kv_row0 = 0;
+    t.valid = search_tile(p, r, &t);
+    return t;
+  }
   // one 32-byte entry of the tile map (built on the device before this kernel)
   const int4* e = reinterpret_cast<const int4*>(p.tile_map) + 2 * r;
   const int4 e0 = e[0], e1 = e[1];

@@ -202,18 +202,22 @@ fa_status enqueue(const fa_plan* plan, void* workspace, void* stream) {
     }
   }
   if (p.varlen) {
-    p.tile_prefix = static_cast<int32_t*>(workspace);
-    p.tile_map = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan->ws_map_off);
-    void* args[] = {(void*)&p.cu_q,           (void*)&p.cu_kv,          (void*)&p.tq,      (void*)&p.tkv,
-                    (void*)&p.nbatch,         (void*)&plan->bm,         (void*)&p.tiles_per_head,
-                    (void*)&p.reverse_tiles,  (void*)&p.tile_prefix,    (void*)&p.tile_map};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::varlen_tile_prefix), dim3(1), dim3(256), args, 0, s);
-    if (e != hipSuccess) return runtime_fail("tile map launch", e);
+    if (!p.tile_search) {
+      p.tile_prefix = static_cast<int32_t*>(workspace);
+      p.tile_map = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan->ws_map_off);
+      void* args[] = {(void*)&p.cu_q,           (void*)&p.cu_kv,          (void*)&p.tq,      (void*)&p.tkv,
+                      (void*)&p.nbatch,         (void*)&plan->bm,         (void*)&p.tiles_per_head,
+                      (void*)&p.reverse_tiles,  (void*)&p.tile_prefix,    (void*)&p.tile_map};
+      hipError_t e =
+          hipLaunchKernel(reinterpret_cast<const void*>(&fa::varlen_tile_prefix), dim3(1), dim3(256), args, 0, s);
+      if (e != hipSuccess) return runtime_fail("tile map launch", e);
+    }
     if (p.has_pse) {
       p.pse_off = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + plan->ws_pse_off);
       void* pargs[] = {(void*)&p.cu_q, (void*)&p.cu_kv, (void*)&p.tq, (void*)&p.tkv, (void*)&p.nbatch, (void*)&p.nq,
                        (void*)&p.pse_off};
-      e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::varlen_pse_prefix), dim3(1), dim3(256), pargs, 0, s);
+      hipError_t e =
+          hipLaunchKernel(reinterpret_cast<const void*>(&fa::varlen_pse_prefix), dim3(1), dim3(256), pargs, 0, s);
       if (e != hipSuccess) return runtime_fail("pse prefix launch", e);
     }
   }

@@ -75,6 +75,7 @@ struct PpCtx {
   const uint8_t* cls_row;  // this group's mask block classes (null: outside a TND mask)
   int skv, row, g_first, g_last;
   int lane, wave, l32, hh;
+  int swave;  // wave index, in a scalar register: the LDS destinations of the loads are scalar
   bool row_ok;
 };
 
@@ -99,23 +100,25 @@ template <typename T, int D, int DR>
 __device__ __forceinline__ void pp_stage_one(char* __restrict__ slot, int jb, const PpCtx<T>& x, int idx) {
   using C = PpCfg<T, D, DR>;
   jb = __builtin_amdgcn_readfirstlane(jb);  // uniform
+  // lane byte offset = the block's first row (uniform) + this lane's row and
+  // unit within the block (loop-invariant); LDS destination uniform
   if (idx < C::K_LOADS) {
     const int unit = 64 * (8 * idx + x.wave) + x.lane;
     const int r = unit / C::KU, u = k_swz<C::KU>(r, unit % C::KU);
-    dma16(x.kbase, x.kn, (lds_void*)(slot + 1024 * (8 * idx + x.wave)),
-          (uint32_t)(jb + r) * (uint32_t)x.krow_b + u * 16);
+    dma16(x.kbase, x.kn, (lds_void*)(slot + 1024 * (8 * idx + x.swave)),
+          (uint32_t)jb * (uint32_t)x.krow_b + ((uint32_t)r * (uint32_t)x.krow_b + u * 16));
   } else if (DR > 0 && idx < C::K_LOADS + C::KR_LOADS) {
     const int n = idx - C::K_LOADS;
     const int unit = 64 * (8 * n + x.wave) + x.lane;
     const int r = unit / C::KRU, u = k_swz<C::KRU>(r, unit % C::KRU);
-    dma16(x.krbase, x.krn, (lds_void*)(slot + C::KR_OFF + 1024 * (8 * n + x.wave)),
-          (uint32_t)(jb + r) * (uint32_t)x.krrow_b + u * 16);
+    dma16(x.krbase, x.krn, (lds_void*)(slot + C::KR_OFF + 1024 * (8 * n + x.swave)),
+          (uint32_t)jb * (uint32_t)x.krrow_b + ((uint32_t)r * (uint32_t)x.krrow_b + u * 16));
   } else {
     const int n = idx - C::K_LOADS - C::KR_LOADS;
     const int unit = 64 * (8 * n + x.wave) + x.lane;
     const int r = unit / C::VU, u = v_swz<C::VU>(r, unit % C::VU);
-    dma16(x.vbase, x.vn, (lds_void*)(slot + C::V_OFF + 1024 * (8 * n + x.wave)),
-          (uint32_t)(jb + r) * (uint32_t)x.vrow_b + u * 16);
+    dma16(x.vbase, x.vn, (lds_void*)(slot + C::V_OFF + 1024 * (8 * n + x.swave)),
+          (uint32_t)jb * (uint32_t)x.vrow_b + ((uint32_t)r * (uint32_t)x.vrow_b + u * 16));
   }
 }
 
@@ -509,6 +512,7 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
   x.g_last = g_last;
   x.lane = lane;
   x.wave = wave;
+  x.swave = __builtin_amdgcn_readfirstlane(wave);
   x.l32 = l32;
   x.hh = hh;
   x.row_ok = row_ok;

@@ -40,6 +40,10 @@ constexpr int kMfmaPpThreads = 512;
 constexpr int kGenericBM = 64;
 constexpr int kGenericBN = 32;
 constexpr int kGenericThreads = 64;
+// TND with at most this many sequences: each workgroup finds its (sequence,
+// query tile) from cu_seqlens_q itself (a wave scans 64 sequences at a time)
+// instead of reading a tile map built by a pre-pass launch.
+constexpr int kTileSearchMaxSeqs = 256;
 
 struct Params {
   // device addresses
@@ -55,8 +59,8 @@ struct Params {
   const float* sink;     // may be null
   const int32_t* cu_q;   // TND only
   const int32_t* cu_kv;  // TND only
-  int32_t* tile_prefix;  // TND only: workspace, [nbatch + 1]
-  int32_t* tile_map;     // TND only: workspace, [tiles_per_head][8] = {b, qt, q0, k0, sq, skv, valid, 0}
+  int32_t* tile_prefix;  // TND without tile_search: workspace, [nbatch + 1]
+  int32_t* tile_map;     // TND without tile_search: workspace, [tiles_per_head][8] = {b, qt, q0, k0, sq, skv, valid, 0}
   const void* pse;       // may be null: additive position bias, q's element type
   int64_t* pse_off;      // TND with pse: workspace, [nbatch + 1] element offset of each sequence's block
   uint8_t* mask_cls;     // with a mask: workspace, class of every (mask slice, 128-row tile, 64-key block)
@@ -96,6 +100,8 @@ struct Params {
   float inv_scale;          // 1 / scale: pse enters the raw score accumulator as pse / scale
 
   int32_t tiles_per_head;   // dense: ceil(sq / BM); TND: ceil(tq / BM) + nbatch (upper bound)
+  int32_t tile_search;      // TND: the kernel finds its tile from cu_seqlens_q (tile_prefix / tile_map unused)
+  int32_t tile_bm;          // TND: query rows per tile
   int32_t num_wg;           // grid size
   int32_t reverse_tiles;    // schedule later (heavier) query tiles first
   int32_t kv_splits;        // dense, 4-wave kernel: workgroups per query tile, each over one key range (1 = off)

@@ -135,12 +135,12 @@ extern "C" int32_t fa_plan_describe(const fa_plan* plan, char* buf, size_t len) 
   const int n = snprintf(buf, len,
                          "kernel=%s dtype=%s d=%d dr=%d dv=%d bm=%d bn=%d grid=%d block=%d ws=%llu "
                          "varlen=%d band=%d pre=%d next=%d mask=%d sink=%d "
-                         "nq=%d nkv=%d tiles_per_head=%d reverse=%d pse=%d pse_lds=%d kv_splits=%d",
+                         "nq=%d nkv=%d tiles_per_head=%d tile_search=%d reverse=%d pse=%d pse_lds=%d kv_splits=%d",
                          plan->kind == fa::KERNEL_MFMA_PP ? "mfma_pp" : (plan->kind == fa::KERNEL_MFMA ? "mfma" : "generic"),
                          dtype_name(plan->dtype), p.d, p.dr,
                          p.dv, plan->bm, plan->bn, p.num_wg, plan->block, (unsigned long long)plan->ws_bytes,
                          p.varlen, p.band, p.pre, p.next, p.has_mask, p.has_sink, p.nq, p.nkv,
-                         p.tiles_per_head, p.reverse_tiles, p.has_pse, p.pse_lds, p.kv_splits);
+                         p.tiles_per_head, p.tile_search, p.reverse_tiles, p.has_pse, p.pse_lds, p.kv_splits);
   return n;
 }
 
@@ -523,17 +523,22 @@ extern "C" fa_status fa_fwd_get_workspace_size(
 
   const int64_t bm = pl->bm;
   int64_t tiles, wg;
-  // Workspace: [tile prefix, int32, TND] [tile map, 8 x int32 per tile, TND]
-  // [pse block offsets, int64, TND with pse] [mask block classes, u8, with a
-  // mask], each part 16-byte aligned.
+  // Workspace: [tile prefix, int32] [tile map, 8 x int32 per tile] (TND with
+  // more than kTileSearchMaxSeqs sequences) [pse block offsets, int64, TND
+  // with pse] [mask block classes, u8, with a mask], each part 16-byte aligned.
   uint64_t ws = 0;
   pl->ws_map_off = pl->ws_pse_off = pl->ws_cls_off = 0;
+  p.tile_search = 0;
+  p.tile_bm = (int32_t)bm;
   if (p.varlen) {
     tiles = cdiv(q.s, bm) + nbatch;
     wg = q.s > 0 ? tiles * q.n : 0;
-    ws = (uint64_t)(nbatch + 1) * sizeof(int32_t);
-    pl->ws_map_off = (ws + 15) / 16 * 16;
-    ws = pl->ws_map_off + (uint64_t)tiles * 8 * sizeof(int32_t);
+    p.tile_search = nbatch <= fa::kTileSearchMaxSeqs;
+    if (!p.tile_search) {
+      ws = (uint64_t)(nbatch + 1) * sizeof(int32_t);
+      pl->ws_map_off = (ws + 15) / 16 * 16;
+      ws = pl->ws_map_off + (uint64_t)tiles * 8 * sizeof(int32_t);
+    }
     if (p.has_pse) {
       pl->ws_pse_off = (ws + 15) / 16 * 16;
       ws = pl->ws_pse_off + (uint64_t)(nbatch + 1) * sizeof(int64_t);

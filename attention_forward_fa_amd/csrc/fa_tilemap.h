@@ -16,15 +16,18 @@
 
 namespace fa {
 
-// Rows [*start, *end) of sequence b: cu[b] and cu[b + 1] clamped into
-// [0, total], the end never before the start.
-FA_HD inline void seq_span(const int32_t* cu, int b, int total, int* start, int* end) {
-  int a = cu[b];
+// Rows [*start, *end) of a sequence whose cumulative lengths are a (before
+// it) and e (after it): a clamped into [0, total], e into [a, total].
+FA_HD inline void clamp_span(int a, int e, int total, int* start, int* end) {
   a = a < 0 ? 0 : (a > total ? total : a);
-  int e = cu[b + 1];
   e = e < a ? a : (e > total ? total : e);
   *start = a;
   *end = e;
+}
+
+// Rows [*start, *end) of sequence b: cu[b] and cu[b + 1] clamped.
+FA_HD inline void seq_span(const int32_t* cu, int b, int total, int* start, int* end) {
+  clamp_span(cu[b], cu[b + 1], total, start, end);
 }
 
 FA_HD inline int seq_rows(const int32_t* cu, int b, int total) {

@@ -150,9 +150,11 @@ typedef int32_t fa_status;
  *   attention_out       output, q's dtype, q's layout with last dim Dv.  Rows
  *                       with no kept key are 0.  Rounded to nearest even.
  *   workspace_size      host out: bytes of device workspace phase 2 needs,
- *                       16-byte aligned parts: for TND the tile prefix
- *                       (4 (B+1) bytes) and a 32-byte tile-map entry per
- *                       tile of the grid, then 8 (B+1) bytes of pse block
+ *                       16-byte aligned parts: for TND with more than 256
+ *                       sequences the tile prefix (4 (B+1) bytes) and a
+ *                       32-byte tile-map entry per tile of the grid (up to
+ *                       256 sequences the kernels find their tiles from
+ *                       cu_seqlens_q themselves), then 8 (B+1) bytes of pse block
  *                       offsets with a TND real_shift; with atten_mask one
  *                       class byte per (mask slice, 128-row tile, 64-key
  *                       block), padded to 16; with a key split (below)

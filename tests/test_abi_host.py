@@ -103,9 +103,30 @@ def test_varlen_plan_workspace():
     smax = desc([N, T, 8], F32)
     st, ws, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND", causal=1, smax=smax, ssum=smax)
     assert st == 0, _lib.last_error_message()
-    assert ws == 80 + 80 * 32  # tile prefix (17 int32 -> 80 bytes) + a 32-byte map entry per tile (64 + 16)
+    # 16 sequences: each workgroup finds its tile from cu_seqlens, no tile map in the workspace
+    assert ws == 0
     d = describe(pl)
     assert "varlen=1" in d and "grid=1920" in d and "reverse=1" in d, d  # (64 + 16) 128-row tiles x 24 heads
+    assert "tile_search=1" in d, d
+    _lib.fa_plan_destroy(pl)
+
+
+def test_varlen_plan_tile_map_beyond_search_limit():
+    """More sequences than the in-kernel search takes: the tile prefix and the
+    map (a 32-byte entry per tile) come back in the workspace."""
+    T, N, B = 8192, 4, 300
+    q = desc([T, N, 128])
+    cu = desc([B + 1], I32)
+    st, ws, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND", causal=1)
+    assert st == 0, _lib.last_error_message()
+    tiles = -(-T // 128) + B
+    assert ws == ((B + 1) * 4 + 15) // 16 * 16 + tiles * 32
+    d = describe(pl)
+    assert "tile_search=0" in d and f"grid={tiles * N}" in d, d
+    _lib.fa_plan_destroy(pl)
+    cu = desc([257], I32)  # 256 sequences: still searched
+    st, ws, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND", causal=1)
+    assert st == 0 and ws == 0 and "tile_search=1" in describe(pl)
     _lib.fa_plan_destroy(pl)
 
 
@@ -310,14 +331,14 @@ def test_mask_class_table_in_workspace():
     assert st == 0 and "kv_splits=4" in describe(pl)
     assert ws == (32 * 63 + 15) // 16 * 16 + 4 * 2 * 4000 * 130 * 4, ws
     _lib.fa_plan_destroy(pl)
-    # TND: tile prefix (6 int32 -> 32 bytes), tile map (8 + 5 tiles x 32 bytes), then the
-    # 2-D mask's table (8 x 11 -> 96)
+    # TND with 5 sequences (tiles found in the kernel, no map): only the 2-D mask's
+    # table (8 x 11 -> 96)
     T, N = 1000, 4
     qt = desc([T, N, 128])
     cu = desc([6], I32)
     st, ws, pl = plan(qt, qt, qt, qt, cuq=cu, cuk=cu, layout=b"TND", mask=desc([1000, 700], U8))
     assert st == 0, _lib.last_error_message()
-    assert ws == 32 + 13 * 32 + 96, ws
+    assert ws == 96, ws  # 5 sequences: no tile map
     _lib.fa_plan_destroy(pl)
     # no mask: no table
     st, ws, pl = plan(q, k, v, o)
@@ -330,9 +351,9 @@ def test_phase2_argument_errors_without_launch():
     assert L.fa_fwd(None, 0, None, None) == 161001
     T, N = 1000, 4
     q = desc([T, N, 128])
-    cu = desc([5], I32)
+    cu = desc([301], I32)  # 300 sequences: a tile map in the workspace
     st, ws, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND")
-    assert st == 0 and ws == 32 + (8 + 4) * 32  # tile prefix (5 int32) + map (12 tiles)
+    assert st == 0 and ws == 1216 + (8 + 300) * 32  # tile prefix (301 int32 -> 1216 bytes) + map (308 tiles)
     assert L.fa_fwd(None, 0, pl, None) == 561201
     assert L.fa_fwd(ctypes.c_void_p(ADDR), ws - 1, pl, None) == 561201
     assert "workspace" in _lib.last_error_message()
@@ -344,7 +365,7 @@ def test_plan_is_not_consumed_by_phase2():
     the same plan answers several phase-2 calls and still describes itself afterwards."""
     L = _lib.lib()
     q = desc([300, 2, 128])
-    cu = desc([3], I32)
+    cu = desc([301], I32)
     st, ws, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND")
     assert st == 0 and ws > 0
     before = describe(pl)
@@ -685,7 +706,7 @@ def test_pse_tnd_workspace():
     cu = desc([6], I32)
     st, ws, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND", pse=desc([12345]))
     assert st == 0, _lib.last_error_message()
-    assert ws == 32 + 13 * 32 + 8 * 6  # tile prefix (6 int32 -> 32 bytes), map (13 tiles), 6 int64 offsets
+    assert ws == 8 * 6  # 5 sequences, no tile map: the 6 int64 pse block offsets
     _lib.fa_plan_destroy(pl)
     st, _, pl = plan(q, q, q, q, cuq=cu, cuk=cu, layout=b"TND", pse=desc([10, 10]))
     assert st == 561103 and pl is None

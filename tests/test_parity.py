@@ -36,6 +36,14 @@ def _report(name, errs):
 # small cases, full comparison
 # ---------------------------------------------------------------------------
 
+def _seq_lengths(n, longest, seed):
+    """n seeded sequence lengths in [0, longest], about one in eight empty."""
+    g = torch.Generator().manual_seed(seed)
+    lens = torch.randint(1, longest + 1, (n,), generator=g)
+    lens[torch.rand(n, generator=g) < 0.125] = 0
+    return lens.tolist()
+
+
 SMALL = {
     "c1_fp32_bnsd": lambda: synth.workload("c1_fp32_bnsd"),
     "c2_small_bf16": lambda: synth.workload("c2_dense_bsnd", "bf16", small=True),
@@ -85,6 +93,13 @@ SMALL = {
                                                      softmax_out_layout="same_as_input"),
     "len_1": lambda: synth.dense_case("x", "BNSD", 1, 2, 1, 128, "bf16", 54),
     "len_63_65": lambda: synth.varlen_case("x", [63, 64, 65, 127, 128, 129], 2, 128, "bf16", 55),
+    # the in-kernel tile search over several 64-sequence chunks (with and
+    # without reversed tiles), and the tile map beyond 256 sequences
+    "seqs_70_causal": lambda: synth.varlen_case("x", _seq_lengths(70, 300, 130), 2, 128, "bf16", 131,
+                                                causal=True),
+    "seqs_130_dense": lambda: synth.varlen_case("x", _seq_lengths(130, 140, 132), 2, 64, "bf16", 133),
+    "seqs_300_tile_map": lambda: synth.varlen_case("x", _seq_lengths(300, 20, 134), 2, 128, "bf16", 135,
+                                                   causal=True),
     "sink_neg_inf": lambda: _sink_neg_inf_case(56),
     "large_logits": lambda: synth.dense_case("x", "BNSD", 1, 2, 200, 128, "bf16", 57, scale=1.0),
     # additive position bias (pse / realShift)

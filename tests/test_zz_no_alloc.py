@@ -1,8 +1,8 @@
 """fa_fwd_noalloc: the same results as fa_fwd, with the library's own scratch array (needs an MI355X).
 
-Each case needs scratch memory: a varlen call (tile prefix and map), a masked
-dense call (mask block classes) and a small dense grid that splits its keys
-(fp32 partial results).  The outputs of fa_fwd_noalloc must equal those of
+Each case needs scratch memory: a varlen call over more than 256 sequences
+(tile prefix and map), a masked dense call (mask block classes) and a small
+dense grid that splits its keys (fp32 partial results).  The outputs of fa_fwd_noalloc must equal those of
 fa_fwd bit for bit; two calls in a row, the second on a smaller input, check
 that what the first left in the array does not leak into the second.
 """
@@ -67,11 +67,18 @@ def _same(a, b):
         assert torch.equal(xi, yi)
 
 
+def _lengths(n, longest, seed):
+    """n seeded sequence lengths in [0, longest]."""
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(0, longest + 1, (n,), generator=g).tolist()
+
+
 CASES = [
-    # varlen, causal, sink: tile prefix and tile map in the scratch
-    ("varlen_big_then_small", lambda: synth.varlen_case("x", [700, 0, 300, 129], 4, 128, "bf16", 140, sink=True,
+    # varlen with more sequences than the kernels' own tile search takes,
+    # causal, sink: tile prefix and tile map in the scratch
+    ("varlen_big_then_small", lambda: synth.varlen_case("x", _lengths(300, 40, 140), 4, 128, "bf16", 140, sink=True,
                                                        causal=True),
-     lambda: synth.varlen_case("x", [65, 1], 2, 128, "bf16", 141, causal=True)),
+     lambda: synth.varlen_case("x", _lengths(260, 10, 141), 2, 128, "bf16", 141, causal=True)),
     # masked dense: mask block classes in the scratch
     ("mask_big_then_small", lambda: synth.dense_case("x", "BNSD", 2, 2, 640, 128, "bf16", 142, mask=True,
                                                      pre_tokens=300, next_tokens=0),
