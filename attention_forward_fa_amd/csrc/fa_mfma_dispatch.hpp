@@ -40,10 +40,13 @@ template <typename T>
 hipError_t launch_mfma_t(const Params& p, hipStream_t s) {
   void* args[] = {const_cast<Params*>(&p)};
   const void* fn = nullptr;
-  // Dv == D, with or without 64 rope dims; D = 256 with Dv = 256 or 128
+  // Dv == D, with or without 64 rope dims; without rope, D in {96, 128, 256}
+  // with any smaller Dv in {64, 96, 128}
   for (const void* f : {mfma_fn_if<T, 128, 0, 128>(p), mfma_fn_if<T, 128, 64, 128>(p), mfma_fn_if<T, 64, 0, 64>(p),
                         mfma_fn_if<T, 64, 64, 64>(p), mfma_fn_if<T, 96, 0, 96>(p), mfma_fn_if<T, 96, 64, 96>(p),
-                        mfma_fn_if<T, 256, 0, 256>(p), mfma_fn_if<T, 256, 0, 128>(p)})
+                        mfma_fn_if<T, 256, 0, 256>(p), mfma_fn_if<T, 256, 0, 128>(p), mfma_fn_if<T, 256, 0, 96>(p),
+                        mfma_fn_if<T, 256, 0, 64>(p), mfma_fn_if<T, 128, 0, 96>(p), mfma_fn_if<T, 128, 0, 64>(p),
+                        mfma_fn_if<T, 96, 0, 64>(p)})
     if (f) fn = f;
   if (!fn) return hipErrorInvalidValue;
   return hipLaunchKernel(fn, dim3(p.num_wg), dim3(kMfmaThreads), args, 0, s);

@@ -356,9 +356,13 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   if (query_rope && kr.ss * esz_in > max_row_b) max_row_b = kr.ss * esz_in;
   const bool block_offsets_fit = (int64_t)fa::kMfmaBN * max_row_b < ((int64_t)1 << 31);
   // (D, Dr, Dv) the four-wave kernel is built for: Dv == D in {64, 96, 128}
-  // with 0 or 64 rope dims; D = 256 (no rope) with Dv = 256 or 128
+  // with 0 or 64 rope dims; without rope, D = 256 with Dv = 256, and D in
+  // {96, 128, 256} with a smaller Dv in {64, 96, 128} (the head dims of the
+  // FAS page's constraints, with the V5 page's kD >= vD)
+  auto dv_ok = [](int64_t d) { return d == 64 || d == 96 || d == 128; };
   const bool dims_mfma = ((dmain == 64 || dmain == 96 || dmain == 128) && v.d == dmain && (drm == 0 || drm == 64)) ||
-                         (dmain == 256 && drm == 0 && (v.d == 256 || v.d == 128));
+                         (dmain == 256 && drm == 0 && v.d == 256) ||
+                         ((dmain == 96 || dmain == 128 || dmain == 256) && drm == 0 && dv_ok(v.d) && v.d < dmain);
   const bool mfma_shape = (dt == FA_DTYPE_F16 || dt == FA_DTYPE_BF16) && dims_mfma && vec_ok(query->data, q) &&
                           vec_ok(key->data, k) &&
                           vec_ok(value->data, v) && vec_ok(attention_out->data, o) &&
@@ -557,8 +561,11 @@ extern "C" fa_status fa_fwd_get_workspace_size(
   p.part_o = p.part_ml = nullptr;
   pl->ws_part_off = 0;
   if (kind == fa::KERNEL_MFMA && !p.varlen && wg > 0 && k.s > 0) {
-    // workgroup slots of the chip: two per CU, one for D = 256 (its LDS stages take 128 KiB)
-    const int64_t slots = dmain == 256 ? fa::kNumCUs : fa::kWgSlots;
+    // workgroup slots of the chip: two per CU while the kernel's LDS (two
+    // K / V stages of 64 rows of Dqk + Dv elements, and the 16 KiB pse tile
+    // when pse goes through LDS) fits in 80 KiB, else one
+    const int64_t lds_b = 2 * (int64_t)fa::kMfmaBN * (dmain + drm + v.d) * esz_in + (p.pse_lds ? 16 * 1024 : 0);
+    const int64_t slots = lds_b <= 80 * 1024 ? fa::kWgSlots : fa::kNumCUs;
     int64_t want = slots / wg;
     if (want > fa::kMaxKvSplits) want = fa::kMaxKvSplits;
     const int64_t max_by_len = k.s / ((int64_t)fa::kMinSplitBlocks * pl->bn);

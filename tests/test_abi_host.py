@@ -589,9 +589,33 @@ def test_dqk_above_dv_on_matrix_cores(dqk, dv, want):
     d = describe(pl)
     assert "kernel=mfma " in d and want in d and f"dv={dv} " in d, d
     _lib.fa_plan_destroy(pl)
-    # with pse (which the rope kernels do not take) or fp32, the generic kernel takes Dv < D as it is
+    # with pse (which the rope kernels do not take) the pair stays as it is: on the matrix cores for
+    # Dqk in {96, 128, 256}, else on the generic kernel
     st, ws, pl = plan(q, q, v, v, pse=desc([1, 4, 512, 512]), layout=b"BSND")
-    assert st == 0 and "kernel=generic" in describe(pl) and f"d={dqk} dr=0" in describe(pl), describe(pl)
+    fam = "kernel=mfma " if dqk in (96, 128, 256) else "kernel=generic"
+    assert st == 0 and fam in describe(pl) and f"d={dqk} dr=0" in describe(pl), describe(pl)
+    _lib.fa_plan_destroy(pl)
+
+
+@pytest.mark.parametrize("dqk,dv", [(96, 64), (128, 96), (256, 96), (256, 64)])
+def test_dqk_above_dv_without_rope_tail(dqk, dv):
+    """Dqk > Dv with Dqk - Dv != 64: the four-wave kernel's own (Dqk, 0, Dv) instantiations, with and
+    without pse; fp32 stays on the generic kernel."""
+    q, v = desc([1, 512, 4, dqk]), desc([1, 512, 4, dv])
+    for pse in (None, desc([1, 4, 512, 512])):
+        st, ws, pl = plan(q, q, v, v, pse=pse, layout=b"BSND")
+        assert st == 0, _lib.last_error_message()
+        d = describe(pl)
+        assert "kernel=mfma " in d and f"d={dqk} dr=0 dv={dv} " in d, d
+        _lib.fa_plan_destroy(pl)
+    qf, vf = desc([1, 512, 4, dqk], F32), desc([1, 512, 4, dv], F32)
+    st, ws, pl = plan(qf, qf, vf, vf)
+    assert st == 0 and "kernel=generic" in describe(pl)
+    _lib.fa_plan_destroy(pl)
+    # a pair outside the instantiated set (Dv above 128 but below Dqk) stays on the generic kernel
+    q2, v2 = desc([1, 512, 4, 256]), desc([1, 512, 4, 192])
+    st, ws, pl = plan(q2, q2, v2, v2)
+    assert st == 0 and "kernel=generic" in describe(pl)
     _lib.fa_plan_destroy(pl)
 
 

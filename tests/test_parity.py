@@ -141,6 +141,17 @@ SMALL = {
     "d256_gqa_fp32": lambda: synth.dense_case("x", "BSND", 1, 4, 90, 256, "fp32", 123, nkv=1, causal=True),
     "d256_dv128_band_mask": lambda: _band_mask_case(124, 70, 9, d=256, dv=128),
     "d256_dv256_mask_blocks_sink": lambda: _block_mask_case(125, 128, 64, (1, 1), d=256, sink=True, skv=400),
+    # Dqk > Dv on the matrix cores (the FAS page's head dims with the V5
+    # page's kD >= vD): 96 -> 64, 128 -> 96 and 128 -> 64 (with pse, where the
+    # rope-tail mapping does not apply), 256 -> 96 and 256 -> 64
+    "d96_dv64_causal": lambda: synth.dense_case("x", "BSND", 1, 2, 190, 96, "bf16", 126, dv=64, causal=True),
+    "d128_dv96_varlen_sink": lambda: synth.varlen_case("x", [130, 0, 257, 64], 2, 128, "bf16", 127, dv=96,
+                                                       sink=True, causal=True),
+    "d128_dv64_pse": lambda: synth.dense_case("x", "BNSD", 1, 2, 200, 128, "fp16", 128, dv=64, pse="full"),
+    "d256_dv96_gqa_fp16": lambda: synth.dense_case("x", "BNSD", 1, 4, 150, 256, "fp16", 129, dv=96, nkv=2,
+                                                   skv=230),
+    "d256_dv64_pse_causal": lambda: synth.dense_case("x", "BNSD", 1, 2, 170, 256, "bf16", 136, dv=64, pse="full",
+                                                     causal=True),
 }
 
 
