@@ -570,6 +570,10 @@ extern "C" fa_status fa_fwd_get_workspace_size(
     if (want > fa::kMaxKvSplits) want = fa::kMaxKvSplits;
     const int64_t max_by_len = k.s / ((int64_t)fa::kMinSplitBlocks * pl->bn);
     if (want > max_by_len) want = max_by_len;
+    // Not with pse: its [Sq, Skv] bias per head dominates the HBM bytes, and
+    // the fp32 partials would add a fifth to them (B1 N8 S4096: 68 MB on 304)
+    // for a few percent of speed.
+    if (real_shift) want = 1;
     if (const char* force = getenv("FA_FWD_KV_SPLIT")) {
       char* end = nullptr;
       const long n = strtol(force, &end, 10);

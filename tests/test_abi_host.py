@@ -450,16 +450,14 @@ def test_family_policy(case, family):
     _lib.fa_plan_destroy(pl)
 
 
-@pytest.mark.parametrize("pse", [False, True])
 @pytest.mark.parametrize("causal", [0, 1])
-def test_small_dense_grid_splits_keys(pse, causal):
+def test_small_dense_grid_splits_keys(causal):
     # B1 N8 S4096: 128 two-group workgroups would leave half the compute units
     # idle; 256 four-wave workgroups fill half the slots, so two key ranges
+    # (with pse there is no split: test_no_key_split_with_pse)
     B, N, S, D = 1, 8, 4096, 128
     q = desc([B, N, S, D])
     kw = dict(layout=b"BNSD", causal=causal, nxt=0 if causal else 2**31 - 1)
-    if pse:
-        kw["pse"] = desc([B, N, S, S])
     st, ws, pl = plan(q, q, q, q, **kw)
     assert st == 0, _lib.last_error_message()
     d = describe(pl)
@@ -773,3 +771,19 @@ def test_merge_validation():
     assert _merge_call([(o, desc([1, 2, 64, 8], BF16), st_)], o) == 161002  # stats dtype
     assert _merge_call([(desc([1, 2, 64, 128], F16), st_, st_)], o) == 161002  # out dtype differs
     assert _merge_call([part], o, layout=b"XYZ") == 161002
+
+def test_no_key_split_with_pse(monkeypatch):
+    """A dense grid too small for the chip splits its keys, except with pse, whose bias dominates the
+    HBM bytes (the split's fp32 partials would add a fifth); FA_FWD_KV_SPLIT still forces a split."""
+    q = desc([1, 8, 4096, 128])
+    st, ws, pl = plan(q, q, q, q, layout=b"BNSD")
+    assert st == 0 and "kv_splits=2" in describe(pl), describe(pl)
+    _lib.fa_plan_destroy(pl)
+    pse = desc([1, 8, 4096, 4096])
+    st, ws, pl = plan(q, q, q, q, pse=pse, layout=b"BNSD")
+    assert st == 0 and "kv_splits=1" in describe(pl) and "pse_lds=1" in describe(pl) and ws == 0, describe(pl)
+    _lib.fa_plan_destroy(pl)
+    monkeypatch.setenv("FA_FWD_KV_SPLIT", "2")
+    st, ws, pl = plan(q, q, q, q, pse=pse, layout=b"BNSD")
+    assert st == 0 and "kv_splits=2" in describe(pl) and ws > 0, describe(pl)
+    _lib.fa_plan_destroy(pl)
