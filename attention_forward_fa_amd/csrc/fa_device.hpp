@@ -10,6 +10,23 @@
 
 namespace fa {
 
+// The output rows and statistics (written once, read by no later tile) are
+// stored with the non-temporal hint, so that they do not push out of the L2
+// the K / V lines other tiles of the head read again (B4 N32 S8192 with a
+// 2048-key window: 1334 MB fetched per call instead of 1635 MB, for 872 MB of
+// algorithmic reads).  The Q loads keep the default policy: loaded
+// non-temporally they arrive later, and short tiles wait on them (8% on
+// 16 sequences of T = 8192).
+typedef unsigned nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void nt_store16(void* p, uint4 u) {
+  __builtin_nontemporal_store(nt_u32x4{u.x, u.y, u.z, u.w}, reinterpret_cast<nt_u32x4*>(p));
+}
+// four copies of a (16 bytes, 16-byte aligned)
+__device__ __forceinline__ void nt_store4f(float* p, float a) {
+  __builtin_nontemporal_store(nt_f32x4{a, a, a, a}, reinterpret_cast<nt_f32x4*>(p));
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();

@@ -153,7 +153,7 @@ __device__ __forceinline__ void o_tile_store(char* __restrict__ lds, const f32x1
   for (int idx = threadIdx.x; idx < nrows * U; idx += NTHREADS) {
     const int r = idx / U, u = idx - r * U;
     const uint4 v = *reinterpret_cast<const uint4*>(lds + (r * U + o_swz<U>(r, u)) * 16);
-    *reinterpret_cast<uint4*>(obase + r * o_ss + 8 * u) = v;
+    nt_store16(obase + r * o_ss + 8 * u, v);
   }
 }
 
@@ -665,8 +665,8 @@ __global__ void __launch_bounds__(kMfmaThreads, (MfmaCfg<T, D, DR, DV>::OCC)) fa
     const int64_t so = tl.b * p.st_sb + tl.h * p.st_sh + orow * p.st_ss + 4 * hh;
     const float mnat = m_max == kNegInf ? kNegInf : m_max * kLn2;
     const float ltrue = lref > 0.f ? lref * fast_exp2(m_ref - m_max) : 0.f;
-    if (p.smax) *reinterpret_cast<float4*>(p.smax + so) = make_float4(mnat, mnat, mnat, mnat);
-    if (p.ssum) *reinterpret_cast<float4*>(p.ssum + so) = make_float4(ltrue, ltrue, ltrue, ltrue);
+    if (p.smax) nt_store4f(p.smax + so, mnat);
+    if (p.ssum) nt_store4f(p.ssum + so, ltrue);
   }
 }
 

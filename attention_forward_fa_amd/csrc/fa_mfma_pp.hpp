@@ -593,8 +593,8 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
     const int64_t so = tl.b * p.st_sb + tl.h * p.st_sh + orow * p.st_ss + 4 * hh;
     const float mnat = m_max == kNegInf ? kNegInf : m_max * kLn2;
     const float ltrue = lref > 0.f ? lref * fast_exp2(m_ref - m_max) : 0.f;
-    if (p.smax) *reinterpret_cast<float4*>(p.smax + so) = make_float4(mnat, mnat, mnat, mnat);
-    if (p.ssum) *reinterpret_cast<float4*>(p.ssum + so) = make_float4(ltrue, ltrue, ltrue, ltrue);
+    if (p.smax) nt_store4f(p.smax + so, mnat);
+    if (p.ssum) nt_store4f(p.ssum + so, ltrue);
   }
 }
 
