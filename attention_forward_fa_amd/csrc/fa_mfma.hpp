@@ -157,6 +157,55 @@ __device__ __forceinline__ void o_tile_store(char* __restrict__ lds, const f32x1
   }
 }
 
+// s_waitcnt lgkmcnt(n) (n <= 8), vector memory and export counters untouched.
+__device__ __forceinline__ void lgkm_wait(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0xc07f); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0xc17f); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0xc27f); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0xc37f); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0xc47f); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0xc57f); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0xc67f); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0xc77f); break;
+    default: __builtin_amdgcn_s_waitcnt(0xc87f); break;
+  }
+}
+
+// One stretch of N matrix instructions that each take one LDS operand:
+// operand m comes from read(m) (OPS LDS instructions) and goes to use(m, .).
+// Reads run kStreamAhead instructions ahead and are issued two at a time, so
+// one wait covers a pair of MFMAs; the sched_group_barrier sequence keeps the
+// compiler from moving the reads back next to their use (where each pair
+// would wait out the whole LDS latency).
+constexpr int kStreamAhead = 4;
+
+template <int N, int OPS, typename V8, typename Read, typename Use>
+__device__ __forceinline__ void mfma_stream(Read&& read, Use&& use) {
+  static_assert(N % 2 == 0 && kStreamAhead % 2 == 0, "pairs");
+  constexpr int A = kStreamAhead < N ? kStreamAhead : N;
+  V8 a[N];
+#pragma unroll
+  for (int m = 0; m < A; ++m) a[m] = read(m);
+#pragma unroll
+  for (int j = 0; j < N; j += 2) {
+    int outstanding = 0;  // reads of MFMAs j + 2 .. j + A - 1 may still fly
+#pragma unroll
+    for (int m = j + 2; m < j + A && m < N; ++m) outstanding += OPS;
+    lgkm_wait(outstanding);
+    use(j, a[j]);
+    use(j + 1, a[j + 1]);
+    if (j + A < N) a[j + A] = read(j + A);
+    if (j + A + 1 < N) a[j + A + 1] = read(j + A + 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, A * OPS, 0);
+#pragma unroll
+  for (int j = 0; j < N; j += 2) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (j + A < N) __builtin_amdgcn_sched_group_barrier(0x100, 2 * OPS, 0);
+  }
+}
+
 // Per-workgroup constants of the key loop.
 template <typename T>
 struct LoopCtx {
@@ -428,11 +477,11 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
   // one in its softmax, which fills the gaps (4-6% on short varlen and small
   // dense grids).
   __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-  for (int ks = 1; ks < C::NKS; ++ks) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) sacc[t] = mfma32<T>(kfrag(ks, t), qf[ks], sacc[t]);
-  }
+  // k-steps 1 .. NKS - 1, the two 32-key tiles alternating
+  mfma_stream<2 * (C::NKS - 1), 1, V8>([&](int m) { return kfrag(1 + (m >> 1), m & 1); },
+                                       [&](int m, const V8& a) {
+                                         sacc[m & 1] = mfma32<T>(a, qf[1 + (m >> 1)], sacc[m & 1]);
+                                       });
   __builtin_amdgcn_s_setprio(0);
 
   // ---- online softmax (per lane: one query row, 32 of the block's keys)
@@ -475,29 +524,28 @@ __device__ __forceinline__ void key_block(const char* __restrict__ cur, char* __
   lsum += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
   __builtin_amdgcn_s_setprio(1);
-  // ---- O^T += V^T P^T.  V^T operand: lane group q = lane / 16 covers output
-  // columns 32 dt + 16 (q & 1) + 0..15 and keys kb = 32 t + 16 s2 + 4 (q >> 1)
-  // (+8 for the second read); lane j of the group points at row kb + j / 4,
-  // columns 4 (j % 4) .. +3 of that 16-column span.
+  // ---- O^T += V^T P^T.  MFMA m: output tile dt = m % NDT, key step (t, s2) =
+  // m / NDT, so consecutive MFMAs accumulate into different tiles.  V^T
+  // operand: lane group q = lane / 16 covers output columns 32 dt + 16 (q & 1)
+  // + 0..15 and keys kb = 32 t + 16 s2 + 4 (q >> 1) (+8 for the second read);
+  // lane j of the group points at row kb + j / 4, columns 4 (j % 4) .. +3 of
+  // that 16-column span.
   const int vq = x.lane >> 4, vj = x.lane & 15;
-#pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt) {
+  auto vread = [&](int m) {
+    const int dt = m % C::NDT, t = (m / C::NDT) >> 1, s2 = (m / C::NDT) & 1;
     const int vu = 4 * dt + 2 * (vq & 1) + ((vj & 3) >> 1);  // logical unit of this lane's 4 columns
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int r0 = 32 * t + 16 * s2 + 4 * (vq >> 1) + (vj >> 2);
-        const int r1 = r0 + 8;
-        const char* a0 = cur + C::V_OFF + (r0 * C::VU + v_swz<C::VU>(r0, vu)) * 16 + 8 * (vj & 1);
-        const char* a1 = cur + C::V_OFF + (r1 * C::VU + v_swz<C::VU>(r1, vu)) * 16 + 8 * (vj & 1);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
-        const V8 a = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[dt] = mfma32<T>(a, pk[t][s2], oacc[dt]);
-      }
-    }
-  }
+    const int r0 = 32 * t + 16 * s2 + 4 * (vq >> 1) + (vj >> 2);
+    const int r1 = r0 + 8;
+    const char* a0 = cur + C::V_OFF + (r0 * C::VU + v_swz<C::VU>(r0, vu)) * 16 + 8 * (vj & 1);
+    const char* a1 = cur + C::V_OFF + (r1 * C::VU + v_swz<C::VU>(r1, vu)) * 16 + 8 * (vj & 1);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
+    return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  mfma_stream<4 * C::NDT, 2, V8>(vread, [&](int m, const V8& a) {
+    const int ts = m / C::NDT;
+    oacc[m % C::NDT] = mfma32<T>(a, pk[ts >> 1][ts & 1], oacc[m % C::NDT]);
+  });
   __builtin_amdgcn_s_setprio(0);
 }
 

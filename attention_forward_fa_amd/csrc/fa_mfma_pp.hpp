@@ -154,21 +154,6 @@ __device__ __forceinline__ void pp_scores(const char* __restrict__ slot, const P
 // LDS operand reads run this many MFMAs ahead in the M phase.
 constexpr int kPpAhead = 4;
 
-// s_waitcnt lgkmcnt(n) (n <= 8), vector memory and export counters untouched.
-__device__ __forceinline__ void pp_wait_lgkm(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0xc07f); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0xc17f); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0xc27f); break;
-    case 3: __builtin_amdgcn_s_waitcnt(0xc37f); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0xc47f); break;
-    case 5: __builtin_amdgcn_s_waitcnt(0xc57f); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0xc67f); break;
-    case 7: __builtin_amdgcn_s_waitcnt(0xc77f); break;
-    default: __builtin_amdgcn_s_waitcnt(0xc87f); break;
-  }
-}
-
 // The M phase as one stream of MFMAs: the score MFMAs of the block in kslot
 // (when do_s), then the P V MFMAs of the block in vslot (when do_pv), with
 // every LDS operand read issued kPpAhead MFMAs ahead of its use (the
@@ -235,7 +220,7 @@ __device__ __forceinline__ void pp_mphase(const char* __restrict__ kslot, const 
       int outstanding = 0;  // reads of MFMAs j + 2 .. j + kPpAhead - 1 may still fly
 #pragma unroll
       for (int m = j + 2; m < j + kPpAhead && m < NM; ++m) outstanding += ops(m);
-      pp_wait_lgkm(outstanding);
+      lgkm_wait(outstanding);
       issue_mfma(j);
       issue_mfma(j + 1);
       issue_read(j + kPpAhead);
