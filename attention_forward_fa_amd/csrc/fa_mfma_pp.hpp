@@ -13,9 +13,12 @@
 //   M phase: S_{k+1} = K_{k+1} Q^T   and   O += P_k V_k      (matrix cores)
 //   V phase: P_{k+1} = softmax step of S_{k+1}               (vector ALUs)
 //
-// and the groups are offset by one phase, with a workgroup barrier between
-// phases: while group 0 issues matrix instructions, group 1 does its softmax,
-// then they swap.  The M phase runs at raised wave priority; its LDS operand
+// and the groups are offset by one phase: a step starts with group 0 in its
+// M phase and group 1 in its softmax, then they swap.  Only the end of a step
+// has a workgroup barrier (the K / V ring needs it); within a step each SIMD's
+// two waves run their phases back to back (a barrier between the phases cost
+// 2-4%: its latency, and the wait for the slower group, which the next phase
+// absorbs without it).  The M phase runs at raised wave priority; its LDS operand
 // reads are issued four MFMAs ahead of their use, two MFMAs' reads at a time,
 // so that one wait covers a pair of MFMAs.  Steps whose blocks are full for
 // both groups (no window edge, sequence end or mask) run without the
@@ -152,7 +155,7 @@ __device__ __forceinline__ void pp_scores(const char* __restrict__ slot, const P
 }
 
 // LDS operand reads run this many MFMAs ahead in the M phase.
-constexpr int kPpAhead = 4;
+constexpr int kPpAhead = 6;
 
 // The M phase as one stream of MFMAs: the score MFMAs of the block in kslot
 // (when do_s), then the P V MFMAs of the block in vslot (when do_pv), with
@@ -233,6 +236,7 @@ __device__ __forceinline__ void pp_mphase(const char* __restrict__ kslot, const 
     // the same order for the scheduler: first reads, then per pair two
     // MFMAs, the next pair's reads and any load
     if (kPpAhead == 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    if (kPpAhead == 6) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
     for (int j = 0; j < NM; j += 2) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -384,7 +388,8 @@ __device__ __forceinline__ void pp_step(char* __restrict__ fill, const char* __r
     if (!FAST && k == 0 && act_k) pp_scores<T, D, DR>(cur, x, st.qf, st.sacc);
     if (act_k) pp_softmax<T, D, DR, FAST>(p, x, jb0 + k * BN, st);
   }
-  __builtin_amdgcn_s_barrier();
+  // (no barrier here: nothing the other group does in this step depends on
+  // it, and each SIMD's two waves balance their phases themselves)
   // phase 2k + 1: group 0 = softmax of block k + 1, group 1 = M phase of step k
   if (grp == 0) {
     if (act_k1) pp_softmax<T, D, DR, FAST>(p, x, jb0 + (k + 1) * BN, st);
