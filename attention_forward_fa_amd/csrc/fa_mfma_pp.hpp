@@ -406,7 +406,14 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
   using V8 = typename Vec8<T>::type;
   constexpr int BN = C::BN;
   constexpr int NSLOT = C::NSLOT;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  // The tile's Q goes through LDS (coalesced row loads, then one 16-byte
+  // read per fragment) into the space of the last ring slot and the LDS past
+  // the ring, both unused until the main loop.
+  constexpr int Q_OFF = (NSLOT - 1) * C::SLOT;
+  constexpr int Q_BYTES = kPpBM * D * (int)sizeof(T);
+  constexpr bool kQLds = DR == 0 && Q_OFF + Q_BYTES <= 160 * 1024;
+  constexpr int LDS_ALLOC = kQLds && Q_OFF + Q_BYTES > C::LDS_BYTES ? Q_OFF + Q_BYTES : C::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[LDS_ALLOC];
 
   const Tile tl = map_tile(p, blockIdx.x);
   if (!tl.valid) return;
@@ -423,7 +430,22 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
 
   PpState<T, D, DR> st;
   // ---- Q^T fragments (B operand): lane holds row `row`, dims 16*ks + 8*hh .. +7
-  {
+  const int64_t q_ss_b = p.q_ss * (int64_t)sizeof(T);
+  const bool q_lds = kQLds && q_ss_b >= D * (int64_t)sizeof(T) && q_ss_b * kPpBM < 0x7fffffff;  // uniform
+  if (q_lds) {
+    // the tile's rows [i0, i0 + BM) into LDS, KU units per row, unit u of
+    // row r at k_swz(r, u): load n of wave w fills units [64 (8n + w), +64);
+    // rows past the sequence end fall outside the descriptor and read zeros
+    const T* qt = static_cast<const T*>(p.q) + tl.b * p.q_sb + tl.h * p.q_sh + (tl.q_row0 + i0) * p.q_ss;
+    const int64_t qn = (int64_t)max(min(kPpBM, tl.sq - i0), 0) * q_ss_b;
+    const int sw = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int n = 0; n < kPpBM * C::KU / kPpThreads; ++n) {
+      const int unit = 64 * (8 * n + wave) + lane;
+      const int r = unit / C::KU, u = k_swz<C::KU>(r, unit % C::KU);
+      dma16(qt, qn, (lds_void*)(smem + Q_OFF + 1024 * (8 * n + sw)), (uint32_t)r * (uint32_t)q_ss_b + u * 16);
+    }
+  } else {
     const int64_t qrow = tl.q_row0 + (row_ok ? row : 0);
     const T* qrowp = static_cast<const T*>(p.q) + tl.b * p.q_sb + tl.h * p.q_sh + qrow * p.q_ss;
 #pragma unroll
@@ -440,6 +462,14 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
       }
     }
   }
+  auto q_from_lds = [&]() {  // after the barrier that follows the Q loads
+    if (q_lds) {
+      const int r = row - i0;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        st.qf[ks] = *reinterpret_cast<const V8*>(smem + Q_OFF + (r * C::KU + k_swz<C::KU>(r, 2 * ks + hh)) * 16);
+    }
+  };
 
   // ---- key blocks: the workgroup walks the union of both groups' ranges; a
   // group skips the blocks outside its own range (still meeting every barrier)
@@ -516,13 +546,19 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
     for (int b = 0; b < NSLOT - 1; ++b) pp_stage<T, D, DR>(slot(b), jb0 + b * BN, x);
     __builtin_amdgcn_s_waitcnt(0x0f70 | ((NSLOT - 2) * C::LPB));  // Q fragments and block 0
     __builtin_amdgcn_s_barrier();
+    q_from_lds();
     if (grp == 0 && active(0)) {
       pp_scores<T, D, DR>(slot(0), x, st.qf, st.sacc);
       pp_softmax<T, D, DR>(p, x, jb0, st);
     }
     // all prologue blocks: the loop's operand reads then only ever wait on
-    // loads issued inside the loop, whose targets the compiler can tell apart
-    __builtin_amdgcn_s_waitcnt(0x0f70);
+    // loads issued inside the loop, whose targets the compiler can tell apart;
+    // and every Q read from LDS is done before the loop refills that space
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_barrier();
+  } else {
+    // no key block: the Q loads still land before the epilogue reuses the LDS
+    __builtin_amdgcn_s_waitcnt(0x0070);
     __builtin_amdgcn_s_barrier();
   }
 
