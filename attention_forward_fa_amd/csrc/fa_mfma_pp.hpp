@@ -564,11 +564,14 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
 
   // ---- main loop
   // Steps whose two blocks are full for both groups (inside every row's
-  // window, before the sequence end, no mask) skip the per-block tests:
-  // blocks [f0, f1] of the workgroup's range are full.  Everything here is
-  // uniform over the workgroup, so both groups run the same steps.
+  // window, before the sequence end, and with a mask of the kept class for
+  // both groups' rows) skip the per-block tests: blocks [f0, f1] of the
+  // workgroup's range are full as far as the window goes, and the run of fast
+  // steps ends at the first step whose blocks the mask does not keep whole
+  // (the rest run the general step).  Everything here is uniform over the
+  // workgroup, so both groups run the same steps.
   int f0 = 1, f1 = 0;
-  if (DR == 0 && !p.has_mask && wg_last >= i0 + 128) {
+  if (DR == 0 && wg_last >= i0 + 128) {
     int lo = 0, end = tl.skv;  // full blocks cover keys [lo, end) for both groups
     if (p.band) {
       lo = max(lo, wg_last - p.pre);
@@ -577,7 +580,29 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
     f0 = max(0, (lo - jb0 + BN - 1) / BN);
     f1 = min(nblocks - 1, (end - jb0) / BN - 1);
   }
-  const int fa = max(f0, 1), fb = f1;  // fast steps k with blocks k and k + 1 in [f0, f1], k >= 1
+  int fa = max(f0, 1), fb = f1;  // fast steps k with blocks k and k + 1 in [f0, f1], k >= 1
+  if (DR == 0 && p.has_mask && fb > fa) {
+    // with a mask the fast steps end before the first block of [fa, fb]
+    // that the mask does not keep whole for both groups: each lane checks
+    // one block per pass, and a ballot finds the first such block
+    static_assert(kClsKeys == BN && kClsRows == 128, "mask classes per (group, key block)");
+    const uint8_t* cls_g0 = mask_class_row(p, tl, i0);
+    const uint8_t* cls_g1 = mask_class_row(p, tl, i0 + 128);
+    for (int c = fa; c <= fb; c += 64) {
+      const int kb = c + lane;
+      const int cb = jb0 / BN + kb;  // class column of block kb
+      bool bad = false;
+      if (kb <= fb) {
+        bad = cls_g0 == nullptr || cls_g1 == nullptr || cb >= p.cls_kblocks || cls_g0[cb] != CLS_KEPT ||
+              cls_g1[cb] != CLS_KEPT;
+      }
+      const uint64_t m = __ballot(bad);
+      if (m != 0ull) {
+        fb = c + __ffsll((long long)m) - 2;  // blocks [fa, fb + 1] kept whole
+        break;
+      }
+    }
+  }
   int k = 0;
   auto step_end = [&]() {
     // block k + 2 has landed (all but the newest NSLOT - 3 blocks)

@@ -129,6 +129,7 @@ SMALL = {
     "mask_documents": lambda: _document_mask_case(85),
     "mask_inside_band": lambda: _mask_inside_band_case(86),
     "mask_outside_band": lambda: _mask_outside_band_case(87),
+    "mask_causal_holes": lambda: _mask_causal_holes_case(89),
     "tnd_mask_blocks": lambda: _tnd_block_mask_case(88),
     # a 2-D TND mask smaller than the longer sequences: positions beyond it are excluded
     "tnd_mask_shorter_than_sequence": lambda: _tnd_small_mask_case(89),
@@ -218,6 +219,19 @@ def _mask_outside_band_case(seed):
     j = torch.arange(640).view(1, -1)
     c.atten_mask = (((i // 128) + (j // 64)) % 4 == 0).to(torch.uint8)
     c.pre_tokens, c.next_tokens = 200, 0
+    return c
+
+
+def _mask_causal_holes_case(seed):
+    """An explicit causal mask over 1100 rows (long runs of whole-kept blocks
+    below the diagonal) with three blocks excluded inside the kept part: one
+    for the first 128-row half of a 256-row tile, one for its second half, one
+    for a whole row of blocks; the kept runs end there."""
+    c = synth.dense_case("x", "BNSD", 1, 2, 1100, 128, "bf16", seed)
+    i = torch.arange(1100).view(-1, 1)
+    j = torch.arange(1100).view(1, -1)
+    holes = ((i // 128 == 6) & (j // 64 == 5)) | ((i // 128 == 7) & (j // 64 == 9)) | ((j // 64 == 12) & (i >= 1024))
+    c.atten_mask = ((j > i) | holes).to(torch.uint8)
     return c
 
 
