@@ -18,19 +18,21 @@
 // has a workgroup barrier (the K / V ring needs it); within a step each SIMD's
 // two waves run their phases back to back (a barrier between the phases cost
 // 2-4%: its latency, and the wait for the slower group, which the next phase
-// absorbs without it).  The M phase runs at raised wave priority; its LDS operand
-// reads are issued four MFMAs ahead of their use, two MFMAs' reads at a time,
-// so that one wait covers a pair of MFMAs.  Steps whose blocks are full for
-// both groups (no window edge, sequence end or mask) run without the
-// per-block tests.
+// absorbs without it).  The M phase runs at raised wave priority; its LDS
+// operand reads are issued kPpAhead (six) MFMAs ahead of their use, two MFMAs'
+// reads at a time, so that one wait covers a pair of MFMAs.  Steps whose
+// blocks are full for both groups (no window edge or sequence end, and kept
+// whole by the mask's block classes) run without the per-block tests.
 //
 // K and V: NSLOT slots, block b in slot b % NSLOT.  In step b each group
 // loads its share of block b + NSLOT - 1 during its M phase, the loads spread
 // evenly between the matrix instructions (no softmax phase carries them);
-// block b - 1, whose slot they fill, was read for the last time in step b - 1.  Every step issues the same loads (past
-// the last block they read zeros into a free slot), and the end of each odd
-// phase waits for all but the newest NSLOT - 3 blocks, so block b + 2 is in
-// LDS before phase 2b + 2.
+// block b - 1, whose slot they fill, was read for the last time in step
+// b - 1.  Every step issues the same loads (past the last block they read
+// zeros into a free slot), and the end of each step waits for all but the
+// newest NSLOT - 3 blocks, so block b + 2 is in LDS before step b + 1.  The
+// tile's Q goes through the last slot (and the LDS past the ring) once, in the
+// prologue.
 //
 // Masking (window edge, sequence end, explicit mask) is applied to the
 // scores in the softmax step of the blocks that need it.
