@@ -79,7 +79,67 @@ __device__ __forceinline__ void merge_weights(const MergeParams& mp, int b, int 
   }
 }
 
-// 16-byte path: thread = (row, 8-element chunk); rows of dv / 8 chunks.
+// 16-byte path with a fixed count of NP parts: thread = (row, 8-element
+// chunk).  Every load of the thread (the NP chunks and the NP statistics
+// pairs) is issued before any is used, and the output leaves with the
+// non-temporal hint (nothing reads it again here).
+template <typename T, int NP>
+__global__ void __launch_bounds__(256) fa_merge_vec_np_kernel(const MergeParams mp) {
+  const int cpr = mp.dv / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = t / cpr;
+  const int chunk = (int)(t - r * cpr);
+  const int64_t per_b = (int64_t)mp.nheads * mp.nrows;
+  if (r >= per_b * mp.nbatch) return;
+  const int b = (int)(r / per_b);
+  const int h = (int)((r - b * per_b) / mp.nrows);
+  const int s = (int)(r - b * per_b - (int64_t)h * mp.nrows);
+  uint4 u[NP];
+  float mc[NP], w[NP];
+#pragma unroll
+  for (int c = 0; c < NP; ++c) {
+    const T* oc = static_cast<const T*>(mp.po[c]) + b * mp.po_sb[c] + h * mp.po_sh[c] + s * mp.po_ss[c] + 8 * chunk;
+    u[c] = *reinterpret_cast<const uint4*>(oc);
+    const int64_t si = b * mp.pst_sb[c] + h * mp.pst_sh[c] + s * mp.pst_ss[c];
+    mc[c] = mp.pm[c][si];
+    w[c] = mp.pl[c][si];
+  }
+  float m = kNegInf;
+#pragma unroll
+  for (int c = 0; c < NP; ++c) m = fmaxf(m, mc[c]);
+  float l = 0.f;
+#pragma unroll
+  for (int c = 0; c < NP; ++c) {
+    w[c] = mc[c] == kNegInf ? 0.f : expf(mc[c] - m) * w[c];
+    l += w[c];
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NP; ++c) {
+    const T* e = reinterpret_cast<const T*>(&u[c]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[c], to_f32(e[i]), acc[i]);
+  }
+  T res[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) res[i] = from_f32<T>(acc[i] * inv);
+  T* o = static_cast<T*>(mp.o) + b * mp.o_sb + h * mp.o_sh + s * mp.o_ss + 8 * chunk;
+  nt_store16(o, *reinterpret_cast<const uint4*>(res));
+  if (chunk == 0) {
+    const int64_t so = b * mp.st_sb + h * mp.st_sh + s * mp.st_ss;
+    if (mp.m) {
+      nt_store4f(mp.m + so, m);
+      nt_store4f(mp.m + so + 4, m);
+    }
+    if (mp.l) {
+      nt_store4f(mp.l + so, l);
+      nt_store4f(mp.l + so + 4, l);
+    }
+  }
+}
+
+// 16-byte path, any part count: thread = (row, 8-element chunk); rows of dv / 8 chunks.
 template <typename T>
 __global__ void __launch_bounds__(256) fa_merge_vec_kernel(const MergeParams mp) {
   const int cpr = mp.dv / 8;
@@ -134,13 +194,23 @@ static bool merge_vec_ok(const MergeParams& mp) {
   return stats_ok && (mp.st_sb % 4 == 0) && (mp.st_sh % 4 == 0) && (mp.st_ss % 4 == 0);
 }
 
+template <typename T>
+static const void* merge_vec_fn(int nparts) {
+  switch (nparts) {
+    case 2: return reinterpret_cast<const void*>(&fa_merge_vec_np_kernel<T, 2>);
+    case 3: return reinterpret_cast<const void*>(&fa_merge_vec_np_kernel<T, 3>);
+    case 4: return reinterpret_cast<const void*>(&fa_merge_vec_np_kernel<T, 4>);
+    default: return reinterpret_cast<const void*>(&fa_merge_vec_kernel<T>);
+  }
+}
+
 int merge_launch(const MergeParams& mp, int32_t dtype, void* stream) {
   const int64_t rows = (int64_t)mp.nbatch * mp.nheads * mp.nrows;
   if (rows == 0) return 0;
   void* args[] = {const_cast<MergeParams*>(&mp)};
   const void* fn = nullptr;
-  if (dtype == FA_DTYPE_BF16 && merge_vec_ok<__bf16>(mp)) fn = reinterpret_cast<const void*>(&fa_merge_vec_kernel<__bf16>);
-  if (dtype == FA_DTYPE_F16 && merge_vec_ok<_Float16>(mp)) fn = reinterpret_cast<const void*>(&fa_merge_vec_kernel<_Float16>);
+  if (dtype == FA_DTYPE_BF16 && merge_vec_ok<__bf16>(mp)) fn = merge_vec_fn<__bf16>(mp.nparts);
+  if (dtype == FA_DTYPE_F16 && merge_vec_ok<_Float16>(mp)) fn = merge_vec_fn<_Float16>(mp.nparts);
   if (fn) {
     const int64_t threads = rows * (mp.dv / 8);
     return (int)hipLaunchKernel(fn, dim3((unsigned)((threads + 255) / 256)), dim3(256), args, 0,

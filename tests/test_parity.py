@@ -701,6 +701,24 @@ def test_outer_split_merge(name, kernel):
     _report(f"outer/{name}/{kernel}", errs)
 
 
+@pytest.mark.parametrize("nparts", [2, 3, 5])
+def test_merge_part_counts(nparts):
+    """The merge's fixed-count forms (2, 3, 4 parts; 4 above) and its any-count form (5)."""
+    case = OUTER["sink_causal_fp16"]()
+    S = case.k.shape[2]
+    cuts = [0] + [S * (c + 1) // nparts + (7 if c == 0 else 0) for c in range(nparts - 1)] + [S]
+    print(f"[parity] merge parts={nparts} cuts={cuts}", flush=True)
+    parts = [_gpu_forward(_chunk_case(case, a, b), kv_start=a, sink=(c == 0))
+             for c, (a, b) in enumerate(zip(cuts[:-1], cuts[1:]))]
+    o, smax, ssum = api.merge_partials(parts, layout="BNSD", heads=case.q.shape[1])
+    torch.cuda.synchronize()
+    O, M, L = pu.run_oracle(case)
+    dt = case.q.dtype
+    errs = {"O": pu.check_output(o.cpu(), O, dt), "m": pu.check_stats(smax.cpu(), M, "max", dt),
+            "logl": pu.check_stats(ssum.cpu(), L, "sum", dt)}
+    _report(f"merge/{nparts}", errs)
+
+
 @pytest.mark.parametrize("kernel", ["auto", "generic"])
 def test_outer_split_query_chunk(kernel):
     """Rows [r0, S) with q_start_idx = r0 against all keys equal those rows of the whole causal result."""
