@@ -387,7 +387,6 @@ __device__ __forceinline__ void pp_step(char* __restrict__ fill, const char* __r
     pp_mphase<T, D, DR>(nxt, cur, fill, jfill, act_k1, act_k, x, st.qf, st.pk, st.sacc, st.oacc);
     __builtin_amdgcn_s_setprio(0);
   } else {
-    if (!FAST && k == 0 && act_k) pp_scores<T, D, DR>(cur, x, st.qf, st.sacc);
     if (act_k) pp_softmax<T, D, DR, FAST>(p, x, jb0 + k * BN, st);
   }
   // (no barrier here: nothing the other group does in this step depends on
@@ -542,16 +541,24 @@ __global__ void __launch_bounds__(kPpThreads, 1) fa_fwd_mfma_pp(const Params p) 
   auto slot = [&](int k) { return smem + (k % NSLOT) * C::SLOT; };
 
   // ---- prologue: blocks 0 .. NSLOT - 2 in flight; group 0 runs block 0's
-  // scores and softmax while block 1 lands
+  // scores and softmax while block 1 lands, group 1 block 0's scores
   if (nblocks > 0) {
 #pragma unroll
     for (int b = 0; b < NSLOT - 1; ++b) pp_stage<T, D, DR>(slot(b), jb0 + b * BN, x);
     __builtin_amdgcn_s_waitcnt(0x0f70 | ((NSLOT - 2) * C::LPB));  // Q fragments and block 0
     __builtin_amdgcn_s_barrier();
     q_from_lds();
-    if (grp == 0 && active(0)) {
-      pp_scores<T, D, DR>(slot(0), x, st.qf, st.sacc);
-      pp_softmax<T, D, DR>(p, x, jb0, st);
+    if (active(0)) {
+      if (grp == 0) {
+        __builtin_amdgcn_s_setprio(1);
+        pp_scores<T, D, DR>(slot(0), x, st.qf, st.sacc);
+        __builtin_amdgcn_s_setprio(0);
+        pp_softmax<T, D, DR>(p, x, jb0, st);
+      } else {
+        // group 1's scores of block 0, on the matrix cores while group 0
+        // runs its softmax (group 1's softmax of block 0 opens step 0)
+        pp_scores<T, D, DR>(slot(0), x, st.qf, st.sacc);
+      }
     }
     // all prologue blocks: the loop's operand reads then only ever wait on
     // loads issued inside the loop, whose targets the compiler can tell apart;
