@@ -19,8 +19,9 @@ After the timed region (never inside it) the line also gets: the per-launch
 p10 / p90, a cold-cache figure (each call after 512 MiB are written, so the
 inputs are out of the 256 MiB last-level cache), the shader clock measured
 while the forward runs back to back (``sclk_mhz_under_load``, from the
-library's clock probe), and for the 16-bit dense workloads the same workload
-in the other 16-bit type (``companion``).
+library's clock probe) with the matrix-core peak scaled to that clock
+(``mfma_peak_at_measured_clock``), and for the 16-bit dense workloads the same
+workload in the other 16-bit type (``companion``).
 """
 from __future__ import annotations
 
@@ -39,6 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s + % of MI355X bf16 MFMA peak, B2 S4096 N24 D128"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 HBM_GBPS = 8000.0
+PEAK_CLOCK_MHZ = 2400.0  # the shader clock the published matrix-core peaks assume
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCES = ["fa_mfma.hpp", "fa_mfma_pp.hpp", "fa_mfma_dispatch.hpp", "fa_device.hpp", "fa_params.h", "fa_mfma_bf16.hip",
                   "fa_mfma_f16.hip", "fa_generic.hip", "fa_launch.hip", "fa_merge.hip"]
@@ -464,6 +466,13 @@ def main():
     if not args.no_clock:
         mhz = run.clock_under_load(dev)
         result["sclk_mhz_under_load"] = round(mhz, 1) if mhz else None
+        if mhz and roof["bound"] == "mfma":
+            # the matrix-core peak scaled to the clock the chip held while the forward ran (the published
+            # peak assumes PEAK_CLOCK_MHZ): how much of the matrix-core time the kernel keeps busy, apart
+            # from the box's clock; roofline.frac above stays against the published peak
+            p_clk = peak * mhz / PEAK_CLOCK_MHZ
+            result["mfma_peak_at_measured_clock"] = {"sclk_mhz": round(mhz, 1), "peak": round(p_clk, 1),
+                                                     "unit": "TFLOP/s", "frac": round(roof["achieved"] / p_clk, 4)}
     if args.workload in DTYPE_WORKLOADS and not args.no_companion:
         # the same workload in the other 16-bit type, timed the same way
         other = "fp16" if dtype == "bf16" else "bf16"
