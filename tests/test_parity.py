@@ -421,6 +421,30 @@ def test_noncontiguous_strides():
     plan.close()
 
 
+@pytest.mark.parametrize("kernel", ["pp", "mfma"])
+def test_overlapping_query_rows(kernel):
+    """A query view whose rows overlap (row stride 64 elements < D = 128): the two-group kernel then loads
+    each lane's fragments itself instead of staging the tile's rows through LDS."""
+    B, N, S, D = 1, 2, 600, 128
+    strides = (N * S * 64 + 64, S * 64 + 64, 64, 1)
+    flat = synth.normal((N * S * 64 + 64 + D,), synth.generator(64), "bf16")
+    q = torch.as_strided(flat, (B, N, S, D), strides)
+    case = synth.dense_case("x", "BNSD", B, N, S, D, "bf16", 65)
+    case.q = q
+    print(f"[parity] start overlapping query rows kernel={kernel}", flush=True)
+    qg = torch.as_strided(flat.cuda(), (B, N, S, D), strides)
+    with pu.forced_kernel(kernel):
+        plan = api.attention_forward(qg, case.k.cuda(), case.v.cuda(), layout="BNSD", scale=case.scale,
+                                     return_plan=True)
+    try:
+        assert f"kernel={'mfma_pp' if kernel == 'pp' else 'mfma'} " in plan.describe(), plan.describe()
+        torch.cuda.synchronize()
+        O, _, _ = pu.run_oracle(case)
+        _report(f"overlap/{kernel}", {"O": pu.check_output(plan.out.cpu(), O, torch.bfloat16)})
+    finally:
+        plan.close()
+
+
 def test_misaligned_uses_generic_and_matches():
     g = synth.generator(62)
     flat = synth.normal((1 + 2 * 100 * 2 * 128,), g, "bf16")
