@@ -14,15 +14,15 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-EXE = os.path.join(ROOT, "_build", "tilemap_check")
 
 
 @pytest.fixture(scope="module")
-def exe():
-    os.makedirs(os.path.dirname(EXE), exist_ok=True)
+def exe(tmp_path_factory):
+    # one binary per test process (parallel runs must not overwrite a binary another one executes)
+    out = str(tmp_path_factory.mktemp("tilemap") / "tilemap_check")
     subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-I", os.path.join(ROOT, "attention_forward_fa_amd", "csrc"),
-                    os.path.join(ROOT, "tests", "tilemap_check.cpp"), "-o", EXE], check=True)
-    return EXE
+                    os.path.join(ROOT, "tests", "tilemap_check.cpp"), "-o", out], check=True)
+    return out
 
 
 def run(exe, cq, ck, bm, tq, tkv, reverse):
