@@ -17,9 +17,10 @@ UNBOUNDED = 2**31 - 1
 
 
 def case(layout, q, k, v=None, *, causal=False, mask=False, pre=UNBOUNDED, nxt=UNBOUNDED, qr=None, cu=None):
-    t = lambda s: torch.empty(s, device="meta") if s is not None else None
-    return types.SimpleNamespace(layout=layout, q=t(q), k=t(k), v=t(v or k), q_rope=t(qr), causal=causal,
+    t = lambda s: torch.empty(s, device="meta", dtype=torch.bfloat16) if s is not None else None
+    return types.SimpleNamespace(layout=layout, q=t(q), k=t(k), v=t(v or k), q_rope=t(qr), k_rope=t(qr), causal=causal,
                                  atten_mask=object() if mask else None, pre_tokens=pre, next_tokens=nxt,
+                                 sink=None, pse=None,
                                  cu_seqlens_q=torch.tensor(cu) if cu else None,
                                  cu_seqlens_kv=torch.tensor(cu) if cu else None)
 
@@ -30,6 +31,9 @@ def test_dense_headline():
     assert bench.kept_pairs(c, block=128) == bench.kept_pairs(c) == 2 * 24 * 4096 * 4096
     assert bench.flops_per_pair(c) == 4 * 128
     assert bench.kept_pairs(c, block=128) * bench.flops_per_pair(c) == 412316860416
+    # algorithmic bytes: Q, K, V read once, O written once, 2 x 8 fp32 statistics per row
+    n = 2 * 4096 * 24 * 128 * 2
+    assert bench.algorithmic_bytes(c) == 4 * n + 2 * (2 * 4096 * 24) * 8 * 4 == 213909504
 
 
 def test_causal_and_band_blocks():
